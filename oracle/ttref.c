@@ -1,0 +1,231 @@
+/*
+ * ttref -- the plain fp64 CPU oracle for one block-wise diffusion decoding step.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may call, link or load this
+ * file: only the tests, the smoke check and the benchmark's CPU-baseline leg use it.
+ * It shares no code, header or constant with the HIP library; it decodes its own
+ * inputs and follows the method's plain definition, in double precision, with no
+ * tiling, no online softmax and no reordering beyond what the definition states.
+ *
+ * Sources (page title, then section):
+ *   [GS]  "Nemotron-TwoTower: Diffusion Language Modeling with Pretrained Autoregressive
+ *          Context" (gist.science explainer, English), Technical Summary.
+ *   [SN]  snilld.dk, "NVIDIA aabner for hoej-throughput tekstgenerering med TwoTower
+ *          diffusion over en frossen autoregressiv rygrad".
+ *
+ * Inputs are bf16 bit patterns (uint16) or fp32; every element is widened exactly to
+ * double before any arithmetic.
+ *
+ * Readings where the pages are silent (each listed with its reason in the design notes):
+ *   - one softmax spans the context keys and the block keys together;
+ *   - no mask inside the block, every valid context key is visible to every block query;
+ *   - no positional term, bias or softcap inside the attention; scale 1/sqrt(D);
+ *   - KV head of query head h is floor(h / (Hq/Hkv));
+ *   - confidence = largest softmax probability of the position's full-vocabulary
+ *     distribution at temperature 1; the token is the lowest index attaining the max;
+ *   - "above the threshold" is strict (conf > gamma);
+ *   - if a sequence has masked positions but none clears gamma, its single most
+ *     confident masked position is committed (ties: lowest position).
+ *
+ * Parity pins: every function here is checked against library routines, closed forms
+ * and invariants by the CPU test suite; no function is left unpinned.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define TTREF_F32 0
+#define TTREF_BF16 1
+
+#define TTREF_OK 0
+#define TTREF_EINVAL 1
+#define TTREF_ENOMEM 2
+
+/* Exact widening of one element to double. */
+static double ttref_load(const void *base, size_t idx, int dtype)
+{
+    if (dtype == TTREF_F32)
+        return (double)((const float *)base)[idx];
+    uint32_t bits = ((uint32_t)((const uint16_t *)base)[idx]) << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* Exported so that the tests can pin the decode itself against a library conversion. */
+double ttref_decode(const void *base, size_t idx, int dtype)
+{
+    return ttref_load(base, idx, dtype);
+}
+
+/*
+ * Denoiser block attention of one attention layer ([GS] Methodology > Architecture, and
+ * Generation Process): each of the S block queries of sequence b and query head h attends,
+ * in one softmax, to the context tower's same-layer keys K_ctx[b, 0:ctx_len[b], g] (past
+ * blocks) followed by the block's own keys K_blk[b, 0:S, g] (bidirectional, unmasked).
+ *
+ *   s_j = (q . k_j) / sqrt(D)
+ *   p_j = exp(s_j - max_k s_k) / sum_k exp(s_k - max_k s_k)
+ *   out[b,i,h,:] = sum_j p_j v_j
+ *
+ * Layouts: q[B,S,Hq,D], k_blk/v_blk[B,S,Hkv,D], k_ctx/v_ctx[B,Lmax,Hkv,D], out[B,S,Hq,D]
+ * (double). Context rows at or beyond ctx_len[b] are never read.
+ */
+int ttref_block_denoise_attn(int B, int S, int Hq, int Hkv, int D, int Lmax, int dtype,
+                             const void *q, const void *k_blk, const void *v_blk,
+                             const void *k_ctx, const void *v_ctx, const int32_t *ctx_len,
+                             double *out)
+{
+    if (B < 0 || S < 1 || Hq < 1 || Hkv < 1 || D < 1 || Lmax < 0 || Hq % Hkv != 0)
+        return TTREF_EINVAL;
+    if (dtype != TTREF_F32 && dtype != TTREF_BF16)
+        return TTREF_EINVAL;
+    for (int b = 0; b < B; ++b)
+        if (ctx_len[b] < 0 || ctx_len[b] > Lmax)
+            return TTREF_EINVAL;
+    const int G = Hq / Hkv;
+    const double inv_sqrt_d = 1.0 / sqrt((double)D);
+    int failed = 0;
+
+#pragma omp parallel for collapse(3) schedule(dynamic)
+    for (int b = 0; b < B; ++b)
+        for (int i = 0; i < S; ++i)
+            for (int h = 0; h < Hq; ++h) {
+                const int g = h / G;
+                const int nctx = ctx_len[b];
+                const int n = nctx + S;
+                double *s = (double *)malloc((size_t)n * sizeof(double));
+                double *qv = (double *)malloc((size_t)D * sizeof(double));
+                if (!s || !qv) {
+                    free(s);
+                    free(qv);
+#pragma omp atomic write
+                    failed = 1;
+                    continue;
+                }
+                const size_t qoff = (((size_t)b * S + i) * Hq + h) * D;
+                for (int d = 0; d < D; ++d)
+                    qv[d] = ttref_load(q, qoff + d, dtype);
+                /* scores over [context keys ; block keys] */
+                for (int j = 0; j < n; ++j) {
+                    const void *kbase;
+                    size_t koff;
+                    if (j < nctx) {
+                        kbase = k_ctx;
+                        koff = (((size_t)b * Lmax + j) * Hkv + g) * D;
+                    } else {
+                        kbase = k_blk;
+                        koff = (((size_t)b * S + (j - nctx)) * Hkv + g) * D;
+                    }
+                    double dot = 0.0;
+                    for (int d = 0; d < D; ++d)
+                        dot += qv[d] * ttref_load(kbase, koff + d, dtype);
+                    s[j] = dot * inv_sqrt_d;
+                }
+                /* softmax over all n keys */
+                double mx = s[0];
+                for (int j = 1; j < n; ++j)
+                    if (s[j] > mx)
+                        mx = s[j];
+                double z = 0.0;
+                for (int j = 0; j < n; ++j) {
+                    s[j] = exp(s[j] - mx);
+                    z += s[j];
+                }
+                for (int j = 0; j < n; ++j)
+                    s[j] /= z;
+                /* probability-weighted sum of the values */
+                double *o = out + qoff;
+                for (int d = 0; d < D; ++d)
+                    o[d] = 0.0;
+                for (int j = 0; j < n; ++j) {
+                    const void *vbase;
+                    size_t voff;
+                    if (j < nctx) {
+                        vbase = v_ctx;
+                        voff = (((size_t)b * Lmax + j) * Hkv + g) * D;
+                    } else {
+                        vbase = v_blk;
+                        voff = (((size_t)b * S + (j - nctx)) * Hkv + g) * D;
+                    }
+                    for (int d = 0; d < D; ++d)
+                        o[d] += s[j] * ttref_load(vbase, voff + d, dtype);
+                }
+                free(s);
+                free(qv);
+            }
+    return failed ? TTREF_ENOMEM : TTREF_OK;
+}
+
+/*
+ * Confidence unmasking of one denoising step ([GS] Training and Conditioning > Sampling;
+ * [SN] Blockwise generering i praksis): every still-masked position gets its greedy token
+ * and a confidence; positions whose confidence is above gamma are committed, the rest stay
+ * masked.
+ *
+ * For each masked (b,i), over the full vocabulary row l[0:V]:
+ *   M = max_v l_v;   token = lowest v with l_v == M;   Z = sum_v exp(l_v - M);
+ *   conf = 1 / Z   (the largest softmax probability);   committed = (conf > gamma).
+ * If sequence b has masked positions and none is committed, the masked position with the
+ * largest conf (lowest i on ties) is committed.
+ * Unmasked positions: token = -1, committed = 0, conf = 0, Z = 0. Their rows are not read.
+ * Outputs token_id[B,S] int32, committed[B,S] uint8; conf and Z ([B,S] double) may be NULL.
+ */
+int ttref_commit(int B, int S, int V, int dtype, const void *logits, const uint8_t *mask,
+                 double gamma, int32_t *token_id, uint8_t *committed, double *conf_out,
+                 double *z_out)
+{
+    if (B < 0 || S < 1 || V < 1 || isnan(gamma))
+        return TTREF_EINVAL;
+    if (dtype != TTREF_F32 && dtype != TTREF_BF16)
+        return TTREF_EINVAL;
+
+#pragma omp parallel for schedule(dynamic)
+    for (int b = 0; b < B; ++b) {
+        int any_masked = 0, any_committed = 0;
+        int best_i = -1;
+        double best_conf = -1.0;
+        for (int i = 0; i < S; ++i) {
+            const size_t r = (size_t)b * S + i;
+            if (!mask[r]) {
+                token_id[r] = -1;
+                committed[r] = 0;
+                if (conf_out)
+                    conf_out[r] = 0.0;
+                if (z_out)
+                    z_out[r] = 0.0;
+                continue;
+            }
+            any_masked = 1;
+            const size_t off = r * (size_t)V;
+            double m = ttref_load(logits, off, dtype);
+            int tok = 0;
+            for (int v = 1; v < V; ++v) {
+                const double x = ttref_load(logits, off + v, dtype);
+                if (x > m) {
+                    m = x;
+                    tok = v;
+                }
+            }
+            double z = 0.0;
+            for (int v = 0; v < V; ++v)
+                z += exp(ttref_load(logits, off + v, dtype) - m);
+            const double conf = 1.0 / z;
+            token_id[r] = tok;
+            committed[r] = (uint8_t)(conf > gamma);
+            any_committed |= committed[r];
+            if (conf_out)
+                conf_out[r] = conf;
+            if (z_out)
+                z_out[r] = z;
+            if (conf > best_conf) {
+                best_conf = conf;
+                best_i = i;
+            }
+        }
+        if (any_masked && !any_committed)
+            committed[(size_t)b * S + best_i] = 1;
+    }
+    return TTREF_OK;
+}

@@ -1,0 +1,90 @@
+"""ctypes binding of the fp64 CPU oracle (oracle/ttref.c). TEST INFRASTRUCTURE ONLY.
+
+Arrays are numpy, host memory. bf16 tensors are uint16 bit patterns, fp32 tensors float32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_LIB = None
+_DT = {"f32": 0, "bf16": 1}
+
+
+def lib_path() -> str:
+    return _build.LIB
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        path = os.environ.get("TTREF_LIB")  # the mutation tests point this at a planted-mistake build
+        if path is None:
+            path = _build.LIB
+            if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_build.SRC):
+                _build.build()
+        L = ctypes.CDLL(path)
+        vp, i32 = ctypes.c_void_p, ctypes.c_int
+        L.ttref_block_denoise_attn.argtypes = [i32] * 7 + [vp] * 7
+        L.ttref_block_denoise_attn.restype = i32
+        L.ttref_commit.argtypes = [i32, i32, i32, i32, vp, vp, ctypes.c_double, vp, vp, vp, vp]
+        L.ttref_commit.restype = i32
+        L.ttref_decode.argtypes = [vp, ctypes.c_size_t, i32]
+        L.ttref_decode.restype = ctypes.c_double
+        _LIB = L
+    return _LIB
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check_dtype(a: np.ndarray, dtype: str):
+    want = np.uint16 if dtype == "bf16" else np.float32
+    if a.dtype != want or not a.flags.c_contiguous:
+        raise TypeError(f"expected contiguous {want} array for dtype {dtype}, got {a.dtype}")
+
+
+def ttref_decode(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Widen every element with the oracle's own decode (for pinning it)."""
+    _check_dtype(a, dtype)
+    L = _lib()
+    flat = a.reshape(-1)
+    return np.array([L.ttref_decode(_ptr(flat), i, _DT[dtype]) for i in range(flat.size)])
+
+
+def ttref_block_denoise_attn(B, S, Hq, Hkv, D, Lmax, dtype, q, k_blk, v_blk, k_ctx, v_ctx, ctx_len):
+    """Returns out[B,S,Hq,D] float64."""
+    for t in (q, k_blk, v_blk, k_ctx, v_ctx):
+        _check_dtype(t, dtype)
+    assert q.size == B * S * Hq * D and k_blk.size == B * S * Hkv * D and v_blk.size == k_blk.size
+    assert k_ctx.size == B * Lmax * Hkv * D and v_ctx.size == k_ctx.size
+    ctx = np.ascontiguousarray(ctx_len, dtype=np.int32)
+    assert ctx.size == B
+    out = np.zeros((B, S, Hq, D), dtype=np.float64)
+    rc = _lib().ttref_block_denoise_attn(B, S, Hq, Hkv, D, Lmax, _DT[dtype], _ptr(q), _ptr(k_blk),
+                                         _ptr(v_blk), _ptr(k_ctx), _ptr(v_ctx), _ptr(ctx), _ptr(out))
+    if rc != 0:
+        raise ValueError(f"ttref_block_denoise_attn failed with status {rc}")
+    return out
+
+
+def ttref_commit(B, S, V, dtype, logits, mask, gamma):
+    """Returns (token_id int32[B,S], committed uint8[B,S], conf f64[B,S], Z f64[B,S])."""
+    _check_dtype(logits, dtype)
+    assert logits.size == B * S * V
+    m = np.ascontiguousarray(mask, dtype=np.uint8)
+    assert m.size == B * S
+    tok = np.zeros((B, S), dtype=np.int32)
+    com = np.zeros((B, S), dtype=np.uint8)
+    conf = np.zeros((B, S), dtype=np.float64)
+    z = np.zeros((B, S), dtype=np.float64)
+    rc = _lib().ttref_commit(B, S, V, _DT[dtype], _ptr(logits), _ptr(m), float(gamma), _ptr(tok),
+                             _ptr(com), _ptr(conf), _ptr(z))
+    if rc != 0:
+        raise ValueError(f"ttref_commit failed with status {rc}")
+    return tok, com, conf, z

@@ -1,0 +1,49 @@
+"""Planted mistakes in the oracle must be caught by its pins (CPU only).
+
+Each case copies oracle/ttref.c, applies one plausible slip (a dropped scale, a flipped
+sign, a wrong KV-head index, a transposed layout, values read from K, a dropped block key,
+>= instead of >, a wrong tie rule, a missing fallback), builds that copy into a temporary
+library and runs the pin suite against it in a child process. The suite must fail.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "ttref.c")
+
+MUTANTS = {
+    "no_scale": ("s[j] = dot * inv_sqrt_d;", "s[j] = dot;"),
+    "exp_sign": ("s[j] = exp(s[j] - mx);", "s[j] = exp(mx - s[j]);"),
+    "kv_head_modulo": ("const int g = h / G;", "const int g = h % Hkv;"),
+    "blk_layout_transposed": ("koff = (((size_t)b * S + (j - nctx)) * Hkv + g) * D;",
+                              "koff = ((size_t)b * S + (j - nctx) + (size_t)g * S) * D;"),
+    "values_from_keys": ("vbase = v_ctx;", "vbase = k_ctx;"),
+    "drop_last_block_key": ("const int n = nctx + S;", "const int n = nctx + S - 1;"),
+    "threshold_ge": ("committed[r] = (uint8_t)(conf > gamma);", "committed[r] = (uint8_t)(conf >= gamma);"),
+    "argmax_tie_highest": ("if (x > m) {", "if (x >= m) {"),
+    "fallback_tie_highest": ("if (conf > best_conf) {", "if (conf >= best_conf) {"),
+    "no_fallback": ("if (any_masked && !any_committed)", "if (0)"),
+    "z_sign": ("z += exp(ttref_load(logits, off + v, dtype) - m);",
+               "z += exp(m - ttref_load(logits, off + v, dtype));"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    msrc = tmp_path / "ttref_mutant.c"
+    msrc.write_text(src.replace(old, new))
+    lib = tmp_path / "libttref_mutant.so"
+    subprocess.run(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp", "-w", str(msrc), "-o",
+                    str(lib), "-lm"], check=True)
+    env = dict(os.environ, TTREF_LIB=str(lib), OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout[-2000:]}"
+    assert "failed" in r.stdout, r.stdout[-2000:] + r.stderr[-2000:]
