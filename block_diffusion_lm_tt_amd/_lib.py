@@ -1,0 +1,216 @@
+"""ctypes binding of libtt (include/tt.h). Argument marshalling only.
+
+Every step of the computation runs in the HIP kernels of libtt.so; this module checks
+tensor dtypes, shapes, devices and contiguity, allocates outputs and workspaces with
+torch (device memory plumbing), and passes raw device pointers plus the current HIP
+stream to the C-ABI. There is no fallback: if libtt.so is missing or a call fails, an
+exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Tuple
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libtt.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "tt.h")
+
+TT_F32, TT_BF16 = 0, 1
+STATUS = {0: "TT_OK", 1: "TT_ERR_INVALID_ARG", 2: "TT_ERR_UNSUPPORTED", 3: "TT_ERR_WORKSPACE",
+          4: "TT_ERR_HIP"}
+
+
+class TTError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)}")
+        self.status = status
+
+
+class AttnShape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("S", ctypes.c_int32), ("Hq", ctypes.c_int32),
+                ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32), ("Lmax", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+class ProfileStats(ctypes.Structure):
+    _fields_ = [("attn_calls", ctypes.c_int64), ("attn_total_ms", ctypes.c_double),
+                ("attn_main_ms", ctypes.c_double), ("commit_calls", ctypes.c_int64),
+                ("commit_total_ms", ctypes.c_double), ("commit_reduce_ms", ctypes.c_double)]
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libtt.so (built by block_diffusion_lm_tt_amd/build.py). Raises if it is missing."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"libtt.so not found at {LIB_PATH}; build it first "
+                              "(python -c 'import __graft_entry__ as g; g.build()')")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+        L.tt_version.restype = i32
+        L.tt_version.argtypes = []
+        L.tt_status_str.restype = ctypes.c_char_p
+        L.tt_status_str.argtypes = [i32]
+        L.tt_block_denoise_attn_workspace.restype = sz
+        L.tt_block_denoise_attn_workspace.argtypes = [ctypes.POINTER(AttnShape)]
+        L.tt_block_denoise_attn.restype = i32
+        L.tt_block_denoise_attn.argtypes = [ctypes.POINTER(AttnShape)] + [vp] * 8 + [sz, vp]
+        L.tt_commit_workspace.restype = sz
+        L.tt_commit_workspace.argtypes = [i32, i32, i32, i32]
+        L.tt_commit.restype = i32
+        L.tt_commit.argtypes = [i32, i32, i32, i32, vp, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp]
+        L.tt_profile_enable.restype = i32
+        L.tt_profile_enable.argtypes = [i32]
+        L.tt_profile_reset.restype = i32
+        L.tt_profile_reset.argtypes = []
+        L.tt_profile_read.restype = i32
+        L.tt_profile_read.argtypes = [ctypes.POINTER(ProfileStats)]
+        _LIB = L
+    return _LIB
+
+
+def header_symbols() -> list:
+    """Names of the functions include/tt.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tt_[a-z0-9_]+)\s*\(", text)))
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise TTError(fn, status)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return TT_BF16
+    if t.dtype == torch.float32:
+        return TT_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; libtt takes bfloat16 or float32")
+
+
+def _dev(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (libtt has no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream(device, stream) -> int:
+    torch = _torch()
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return int(s.cuda_stream)
+
+
+def attn_shape(B, S, Hq, Hkv, D, Lmax, dtype_code) -> AttnShape:
+    return AttnShape(B, S, Hq, Hkv, D, Lmax, dtype_code)
+
+
+def tt_block_denoise_attn_workspace(B, S, Hq, Hkv, D, Lmax, dtype_code) -> int:
+    sh = attn_shape(B, S, Hq, Hkv, D, Lmax, dtype_code)
+    return int(lib().tt_block_denoise_attn_workspace(ctypes.byref(sh)))
+
+
+def tt_commit_workspace(B, S, V, dtype_code) -> int:
+    return int(lib().tt_commit_workspace(B, S, V, dtype_code))
+
+
+def tt_block_denoise_attn(q, k_blk, v_blk, k_ctx, v_ctx, ctx_len, out=None, workspace=None,
+                          stream=None):
+    """o[B,S,Hq,D] = denoiser block attention over [context KV ; block KV] (see include/tt.h)."""
+    torch = _torch()
+    for name, t in (("q", q), ("k_blk", k_blk), ("v_blk", v_blk), ("k_ctx", k_ctx), ("v_ctx", v_ctx),
+                    ("ctx_len", ctx_len)):
+        _dev(t, name)
+    B, S, Hq, D = q.shape
+    Bk, Sk, Hkv, Dk = k_blk.shape
+    Lmax = k_ctx.shape[1]
+    if (Bk, Sk, Dk) != (B, S, D) or v_blk.shape != k_blk.shape:
+        raise ValueError("k_blk/v_blk must be [B,S,Hkv,D] matching q")
+    if k_ctx.shape != (B, Lmax, Hkv, D) or v_ctx.shape != k_ctx.shape:
+        raise ValueError("k_ctx/v_ctx must be [B,Lmax,Hkv,D]")
+    if ctx_len.dtype != torch.int32 or ctx_len.shape != (B,):
+        raise ValueError("ctx_len must be int32 [B]")
+    dt = _dtype_code(q)
+    for t in (k_blk, v_blk, k_ctx, v_ctx):
+        if t.dtype != q.dtype:
+            raise TypeError("q, k and v tensors must share one dtype")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    _dev(out, "out")
+    sh = attn_shape(B, S, Hq, Hkv, D, Lmax, dt)
+    need = int(lib().tt_block_denoise_attn_workspace(ctypes.byref(sh)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace")
+    st = lib().tt_block_denoise_attn(ctypes.byref(sh), q.data_ptr(), k_blk.data_ptr(), v_blk.data_ptr(),
+                                     k_ctx.data_ptr(), v_ctx.data_ptr(), ctx_len.data_ptr(), out.data_ptr(),
+                                     workspace.data_ptr(), workspace.numel(), _stream(q.device, stream))
+    _check("tt_block_denoise_attn", st)
+    return out
+
+
+def tt_commit(logits, mask, gamma: float, token_id=None, committed=None, conf=None, workspace=None,
+              stream=None, want_conf: bool = True) -> Tuple:
+    """(token_id int32[B,S], committed uint8[B,S], conf float32[B,S] or None); see include/tt.h."""
+    torch = _torch()
+    _dev(logits, "logits")
+    _dev(mask, "mask")
+    B, S, V = logits.shape
+    if mask.dtype != torch.uint8 or mask.shape != (B, S):
+        raise ValueError("mask must be uint8 [B,S]")
+    dt = _dtype_code(logits)
+    dev = logits.device
+    if token_id is None:
+        token_id = torch.empty((B, S), dtype=torch.int32, device=dev)
+    if committed is None:
+        committed = torch.empty((B, S), dtype=torch.uint8, device=dev)
+    if conf is None and want_conf:
+        conf = torch.empty((B, S), dtype=torch.float32, device=dev)
+    if token_id.dtype != torch.int32 or token_id.shape != (B, S):
+        raise ValueError("token_id must be int32 [B,S]")
+    if committed.dtype != torch.uint8 or committed.shape != (B, S):
+        raise ValueError("committed must be uint8 [B,S]")
+    _dev(token_id, "token_id")
+    _dev(committed, "committed")
+    if conf is not None:
+        if conf.dtype != torch.float32 or conf.shape != (B, S):
+            raise ValueError("conf must be float32 [B,S]")
+        _dev(conf, "conf")
+    need = int(lib().tt_commit_workspace(B, S, V, dt))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _dev(workspace, "workspace")
+    st = lib().tt_commit(B, S, V, dt, logits.data_ptr(), mask.data_ptr(), float(gamma), token_id.data_ptr(),
+                         committed.data_ptr(), conf.data_ptr() if conf is not None else None,
+                         workspace.data_ptr(), workspace.numel(), _stream(dev, stream))
+    _check("tt_commit", st)
+    return token_id, committed, conf
+
+
+def profile_enable(on: bool = True):
+    _check("tt_profile_enable", lib().tt_profile_enable(1 if on else 0))
+
+
+def profile_reset():
+    _check("tt_profile_reset", lib().tt_profile_reset())
+
+
+def profile_read() -> dict:
+    s = ProfileStats()
+    _check("tt_profile_read", lib().tt_profile_read(ctypes.byref(s)))
+    return {k: getattr(s, k) for k, _ in ProfileStats._fields_}

@@ -1,0 +1,267 @@
+// libtt C-ABI: argument validation, workspace layout, launches and kernel timing.
+// The operations themselves are documented in include/tt.h.
+#include <math.h>
+#include <mutex>
+#include <vector>
+
+#include "tt_internal.h"
+
+namespace tt {
+namespace {
+
+constexpr int kCUs = 256;        // MI355X compute units
+constexpr int kWgPerCU = 1;      // resident MFMA-attention workgroups per CU (register bound)
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct AttnPlan {
+  bool mfma;
+  int NQ, NC;
+  size_t plan_bytes, part_bytes;
+};
+
+tt_status plan_attn(const tt_attn_shape* sh, AttnPlan* p) {
+  if (!sh) return TT_ERR_INVALID_ARG;
+  if (sh->B < 0 || sh->S < 1 || sh->Hq < 1 || sh->Hkv < 1 || sh->D < 1 || sh->Lmax < 0)
+    return TT_ERR_INVALID_ARG;
+  if (sh->Hq % sh->Hkv != 0) return TT_ERR_INVALID_ARG;
+  if (sh->dtype != TT_F32 && sh->dtype != TT_BF16) return TT_ERR_UNSUPPORTED;
+  if (sh->D > 256 || sh->S > 1024 || sh->B > kMaxB) return TT_ERR_UNSUPPORTED;
+  const long long lim = 1LL << 31;
+  if ((long long)sh->B * sh->S * sh->Hq * sh->D >= lim) return TT_ERR_UNSUPPORTED;
+  if ((long long)sh->B * sh->Lmax * sh->Hkv * sh->D >= lim) return TT_ERR_UNSUPPORTED;
+  p->mfma = sh->dtype == TT_BF16 && sh->D == kAttnMfmaD;
+  const int G = sh->Hq / sh->Hkv;
+  p->NQ = (G * sh->S + kAttnRowsPerWg - 1) / kAttnRowsPerWg;
+  int nc = (kCUs * kWgPerCU) / p->NQ;
+  nc = nc / 8 * 8;
+  p->NC = nc < 8 ? 8 : nc;
+  if (p->mfma) {
+    p->plan_bytes = align_up((size_t)(sh->B + 1) * sizeof(int32_t));
+    p->part_bytes = align_up((size_t)p->NC * 2 * p->NQ * kAttnRowsPerWg * (kAttnMfmaD + 2) * sizeof(float));
+  } else {
+    p->plan_bytes = p->part_bytes = 0;
+  }
+  return TT_OK;
+}
+
+struct CommitPlan {
+  int n_chunks, chunk_elems;
+  size_t chunk_bytes, row_bytes, done_bytes;
+};
+
+tt_status plan_commit(int32_t B, int32_t S, int32_t V, int32_t dtype, CommitPlan* p) {
+  if (B < 0 || S < 1 || V < 1) return TT_ERR_INVALID_ARG;
+  if (dtype != TT_F32 && dtype != TT_BF16) return TT_ERR_UNSUPPORTED;
+  if (S > 1024) return TT_ERR_UNSUPPORTED;
+  if ((long long)B * S * V >= (1LL << 40)) return TT_ERR_UNSUPPORTED;
+  p->chunk_elems = commit_chunk_elems(dtype);
+  p->n_chunks = (V + p->chunk_elems - 1) / p->chunk_elems;
+  p->chunk_bytes = align_up((size_t)B * S * p->n_chunks * sizeof(CommitChunk));
+  p->row_bytes = align_up((size_t)B * S * sizeof(CommitRow));
+  p->done_bytes = align_up((size_t)B * sizeof(int32_t));
+  return TT_OK;
+}
+
+// ---- timing -------------------------------------------------------------------------
+constexpr int kMaxTimed = 4096;
+
+struct Profiler {
+  std::mutex mu;
+  bool enabled = false;
+  std::vector<hipEvent_t> attn_ev[4];   // attn start, main start, main end, attn end
+  std::vector<hipEvent_t> commit_ev[3]; // commit start, reduce end, commit end
+  int64_t attn_calls = 0, commit_calls = 0;
+  int attn_used = 0, commit_used = 0;
+};
+Profiler g_prof;
+
+hipEvent_t ev_slot(std::vector<hipEvent_t>& v, int idx) {
+  while ((int)v.size() <= idx) {
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    v.push_back(e);
+  }
+  return v[idx];
+}
+
+}  // namespace
+}  // namespace tt
+
+using namespace tt;
+
+extern "C" {
+
+int32_t tt_version(void) { return (1 << 16) | 0; }
+
+const char* tt_status_str(tt_status s) {
+  switch (s) {
+    case TT_OK: return "TT_OK";
+    case TT_ERR_INVALID_ARG: return "TT_ERR_INVALID_ARG";
+    case TT_ERR_UNSUPPORTED: return "TT_ERR_UNSUPPORTED";
+    case TT_ERR_WORKSPACE: return "TT_ERR_WORKSPACE";
+    case TT_ERR_HIP: return "TT_ERR_HIP";
+  }
+  return "TT_UNKNOWN_STATUS";
+}
+
+size_t tt_block_denoise_attn_workspace(const tt_attn_shape* shape) {
+  AttnPlan p;
+  if (plan_attn(shape, &p) != TT_OK) return 0;
+  const size_t n = p.plan_bytes + p.part_bytes;
+  return n < kAlign ? kAlign : n;
+}
+
+tt_status tt_block_denoise_attn(const tt_attn_shape* shape, const void* q, const void* k_blk,
+                                const void* v_blk, const void* k_ctx, const void* v_ctx,
+                                const int32_t* ctx_len, void* o, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  AttnPlan p;
+  tt_status st = plan_attn(shape, &p);
+  if (st != TT_OK) return st;
+  if (shape->B == 0) return TT_OK;
+  if (!q || !k_blk || !v_blk || !ctx_len || !o) return TT_ERR_INVALID_ARG;
+  if (shape->Lmax > 0 && (!k_ctx || !v_ctx)) return TT_ERR_INVALID_ARG;
+  const size_t need = tt_block_denoise_attn_workspace(shape);
+  if (!workspace || workspace_bytes < need) return TT_ERR_WORKSPACE;
+
+  AttnArgs a;
+  a.q = q;
+  a.k_blk = k_blk;
+  a.v_blk = v_blk;
+  a.k_ctx = k_ctx;
+  a.v_ctx = v_ctx;
+  a.ctx_len = ctx_len;
+  a.o = o;
+  a.plan = static_cast<int32_t*>(workspace);
+  a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.plan_bytes);
+  a.B = shape->B;
+  a.S = shape->S;
+  a.Hq = shape->Hq;
+  a.Hkv = shape->Hkv;
+  a.G = shape->Hq / shape->Hkv;
+  a.D = shape->D;
+  a.Lmax = shape->Lmax;
+  a.NQ = p.NQ;
+  a.NC = p.NC;
+  a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)shape->D));
+
+  hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
+  {
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    if (g_prof.enabled) {
+      ++g_prof.attn_calls;
+      if (g_prof.attn_used < kMaxTimed) {
+        for (int k = 0; k < 4; ++k) ev[k] = ev_slot(g_prof.attn_ev[k], g_prof.attn_used);
+        if (ev[0] && ev[1] && ev[2] && ev[3]) ++g_prof.attn_used;
+        else ev[0] = ev[1] = ev[2] = ev[3] = nullptr;
+      }
+    }
+  }
+  if (ev[0]) (void)hipEventRecord(ev[0], stream);
+  hipError_t e;
+  if (p.mfma) {
+    e = launch_attn_mfma(a, stream, ev[1], ev[2]);
+  } else {
+    if (ev[1]) (void)hipEventRecord(ev[1], stream);
+    e = launch_attn_generic(a, shape->dtype, stream);
+    if (ev[2]) (void)hipEventRecord(ev[2], stream);
+  }
+  if (ev[3]) (void)hipEventRecord(ev[3], stream);
+  return e == hipSuccess ? TT_OK : TT_ERR_HIP;
+}
+
+size_t tt_commit_workspace(int32_t B, int32_t S, int32_t V, int32_t dtype) {
+  CommitPlan p;
+  if (plan_commit(B, S, V, dtype, &p) != TT_OK) return 0;
+  const size_t n = p.chunk_bytes + p.row_bytes + p.done_bytes;
+  return n < kAlign ? kAlign : n;
+}
+
+tt_status tt_commit(int32_t B, int32_t S, int32_t V, int32_t dtype, const void* logits,
+                    const uint8_t* mask, float gamma, int32_t* token_id, uint8_t* committed,
+                    float* conf, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  CommitPlan p;
+  tt_status st = plan_commit(B, S, V, dtype, &p);
+  if (st != TT_OK) return st;
+  if (isnan(gamma)) return TT_ERR_INVALID_ARG;
+  if (B == 0) return TT_OK;
+  if (!logits || !mask || !token_id || !committed) return TT_ERR_INVALID_ARG;
+  const size_t need = tt_commit_workspace(B, S, V, dtype);
+  if (!workspace || workspace_bytes < need) return TT_ERR_WORKSPACE;
+
+  CommitArgs a;
+  a.logits = logits;
+  a.mask = mask;
+  a.gamma = gamma;
+  a.token_id = token_id;
+  a.committed = committed;
+  a.conf = conf;
+  char* ws = static_cast<char*>(workspace);
+  a.chunks = reinterpret_cast<CommitChunk*>(ws);
+  a.rows = reinterpret_cast<CommitRow*>(ws + p.chunk_bytes);
+  a.seq_done = reinterpret_cast<int32_t*>(ws + p.chunk_bytes + p.row_bytes);
+  a.B = B;
+  a.S = S;
+  a.V = V;
+  a.n_chunks = p.n_chunks;
+  a.chunk_elems = p.chunk_elems;
+  a.dtype = dtype;
+
+  hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+  {
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    if (g_prof.enabled) {
+      ++g_prof.commit_calls;
+      if (g_prof.commit_used < kMaxTimed) {
+        for (int k = 0; k < 3; ++k) ev[k] = ev_slot(g_prof.commit_ev[k], g_prof.commit_used);
+        if (ev[0] && ev[1] && ev[2]) ++g_prof.commit_used;
+        else ev[0] = ev[1] = ev[2] = nullptr;
+      }
+    }
+  }
+  hipError_t e = launch_commit(a, stream, ev[0], ev[1]);
+  if (ev[2]) (void)hipEventRecord(ev[2], stream);
+  return e == hipSuccess ? TT_OK : TT_ERR_HIP;
+}
+
+tt_status tt_profile_enable(int32_t enable) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  g_prof.enabled = enable != 0;
+  return TT_OK;
+}
+
+tt_status tt_profile_reset(void) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  g_prof.attn_calls = g_prof.commit_calls = 0;
+  g_prof.attn_used = g_prof.commit_used = 0;
+  return TT_OK;
+}
+
+tt_status tt_profile_read(tt_profile_stats* out) {
+  if (!out) return TT_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  tt_profile_stats s = {};
+  float ms = 0.0f;
+  for (int k = 0; k < g_prof.attn_used; ++k) {
+    if (hipEventSynchronize(g_prof.attn_ev[3][k]) != hipSuccess) return TT_ERR_HIP;
+    if (hipEventElapsedTime(&ms, g_prof.attn_ev[0][k], g_prof.attn_ev[3][k]) != hipSuccess) return TT_ERR_HIP;
+    s.attn_total_ms += ms;
+    if (hipEventElapsedTime(&ms, g_prof.attn_ev[1][k], g_prof.attn_ev[2][k]) != hipSuccess) return TT_ERR_HIP;
+    s.attn_main_ms += ms;
+  }
+  for (int k = 0; k < g_prof.commit_used; ++k) {
+    if (hipEventSynchronize(g_prof.commit_ev[2][k]) != hipSuccess) return TT_ERR_HIP;
+    if (hipEventElapsedTime(&ms, g_prof.commit_ev[0][k], g_prof.commit_ev[2][k]) != hipSuccess) return TT_ERR_HIP;
+    s.commit_total_ms += ms;
+    if (hipEventElapsedTime(&ms, g_prof.commit_ev[0][k], g_prof.commit_ev[1][k]) != hipSuccess) return TT_ERR_HIP;
+    s.commit_reduce_ms += ms;
+  }
+  s.attn_calls = g_prof.attn_used;
+  s.commit_calls = g_prof.commit_used;
+  *out = s;
+  return TT_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,27 @@
+"""Move seeded host inputs (numpy, bf16 as uint16 bits) onto the GPU as torch tensors."""
+from __future__ import annotations
+
+import numpy as np
+
+from . import workloads as W
+
+
+def to_torch(a: np.ndarray, dtype: str, device):
+    import torch
+    if dtype == W.BF16:
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(device)
+
+
+def attn_to_device(x: W.AttnInputs, device):
+    import torch
+    f = lambda a: to_torch(a, x.dtype, device)  # noqa: E731
+    return (f(x.q), f(x.k_blk), f(x.v_blk), f(x.k_ctx), f(x.v_ctx),
+            torch.from_numpy(np.ascontiguousarray(x.ctx_len, dtype=np.int32)).to(device))
+
+
+def commit_to_device(c: W.CommitInputs, device):
+    import torch
+    return to_torch(c.logits, c.dtype, device), torch.from_numpy(np.ascontiguousarray(c.mask)).to(device)

@@ -1,0 +1,156 @@
+/*
+ * libtt -- the hot path of one block-wise diffusion decoding step, for AMD Instinct MI355X
+ * (gfx950): the denoiser's block attention over its own block KV plus the frozen context
+ * tower's same-layer KV, and the confidence-threshold (gamma) commit.
+ *
+ * Method source: "Nemotron-TwoTower: Diffusion Language Modeling with Pretrained
+ * Autoregressive Context" (gist.science explainer, English), Technical Summary; and the
+ * snilld.dk article on TwoTower (sections "Hvad TwoTower aendrer teknisk" and "Blockwise
+ * generering i praksis").
+ *
+ * Conventions for every call
+ *   - All tensor pointers are DEVICE pointers to caller-owned, contiguous, row-major memory
+ *     (last index fastest). The library keeps no pointer after a call returns.
+ *   - Calls are asynchronous on the given stream (a hipStream_t; NULL = the default stream).
+ *     Host-side validation runs before any launch and never synchronizes. Kernel execution
+ *     errors surface at the caller's next synchronization.
+ *   - The library allocates no device memory. Scratch space comes from the caller as a
+ *     workspace whose minimum size the matching *_workspace() query returns; its contents
+ *     on entry are irrelevant, and a workspace must not be shared by calls that may run
+ *     concurrently.
+ *   - Outputs must not alias inputs or the workspace.
+ *   - Element types: TT_F32 is IEEE binary32; TT_BF16 is bfloat16 (the upper 16 bits of a
+ *     binary32), passed as 16-bit words.
+ */
+#ifndef TT_H
+#define TT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TT_OK = 0,
+    TT_ERR_INVALID_ARG = 1, /* null pointer, negative or inconsistent size, NaN gamma    */
+    TT_ERR_UNSUPPORTED = 2, /* a size or dtype outside the supported set listed below    */
+    TT_ERR_WORKSPACE = 3,   /* workspace pointer null or smaller than the query returned */
+    TT_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed                */
+} tt_status;
+
+typedef enum { TT_F32 = 0, TT_BF16 = 1 } tt_dtype;
+
+/* Shape of one attention call. B sequences, S block positions, Hq query heads sharing
+ * Hkv KV heads (Hq % Hkv == 0; query head h reads KV head h / (Hq/Hkv)), head dim D,
+ * and Lmax rows of context KV storage per sequence. */
+typedef struct {
+    int32_t B, S, Hq, Hkv, D, Lmax;
+    int32_t dtype; /* tt_dtype */
+} tt_attn_shape;
+
+/* Library version, (major << 16) | minor. */
+int32_t tt_version(void);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *tt_status_str(tt_status s);
+
+/* ---------------------------------------------------------------------------------------
+ * tt_block_denoise_attn -- denoiser block attention of one attention layer.
+ *
+ * Defined by Nemotron-TwoTower (gist.science explainer), Technical Summary > Methodology >
+ * Architecture (bidirectional attention inside the noisy block, cross-attention to the
+ * same layer of the frozen context tower) and > Generation Process (at each layer the
+ * denoiser attends to the context tower's KV cache of past blocks and to its own KV cache
+ * of the current block). One softmax spans both key sets:
+ *
+ *   keys(b, g)   = [ k_ctx[b, 0:ctx_len[b], g, :] ; k_blk[b, 0:S, g, :] ]   (same for values)
+ *   o[b,i,h,:]   = softmax_j( q[b,i,h,:] . keys_j / sqrt(D) ) @ values,   g = h / (Hq/Hkv)
+ *
+ * No mask inside the block, no positional term, no bias. Accumulation is fp32; the output
+ * has the input dtype (bf16 rounded to nearest even).
+ *
+ *   q        [B, S, Hq, D]      dtype                   (device, read)
+ *   k_blk    [B, S, Hkv, D]     dtype                   (device, read)
+ *   v_blk    [B, S, Hkv, D]     dtype                   (device, read)
+ *   k_ctx    [B, Lmax, Hkv, D]  dtype                   (device, read)
+ *   v_ctx    [B, Lmax, Hkv, D]  dtype                   (device, read)
+ *   ctx_len  [B]                int32, 0 <= ctx_len[b] <= Lmax   (device, read)
+ *   o        [B, S, Hq, D]      dtype                   (device, written)
+ * Context rows at or beyond ctx_len[b] are never read and may hold anything (NaN included).
+ * ctx_len lives on the device, so the host cannot check it; the kernels clamp each value
+ * into [0, Lmax] before use (a value outside that range is a caller error, not a fault).
+ *
+ * Supported: dtype TT_BF16 or TT_F32; 1 <= D <= 256 (D == 128 with bf16 takes the MFMA
+ * path); 1 <= S <= 1024; B*S*Hq*D, B*Lmax*Hkv*D < 2^31; B <= 16383. Anything else returns
+ * TT_ERR_UNSUPPORTED. B == 0 is a no-op. k_ctx/v_ctx may be NULL only when Lmax == 0.
+ * ------------------------------------------------------------------------------------- */
+size_t tt_block_denoise_attn_workspace(const tt_attn_shape *shape);
+
+tt_status tt_block_denoise_attn(const tt_attn_shape *shape, const void *q, const void *k_blk,
+                                const void *v_blk, const void *k_ctx, const void *v_ctx,
+                                const int32_t *ctx_len, void *o, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * tt_commit -- confidence unmasking of one denoising step.
+ *
+ * Defined by Nemotron-TwoTower (gist.science explainer), Technical Summary > Training and
+ * Conditioning > Sampling (all masked tokens are predicted at once; those whose confidence
+ * is above gamma are committed, the rest stay masked) and the snilld.dk TwoTower article,
+ * "Blockwise generering i praksis" (a lower gamma commits more tokens per step).
+ *
+ * For every masked position (b,i) over its full vocabulary row l[0:V]:
+ *   token = lowest v with l_v == max l;  Z = sum_v exp(l_v - max l);  conf = 1/Z;
+ *   committed = conf > gamma   (strict).
+ * If sequence b has masked positions and none is committed, its masked position with the
+ * largest conf (lowest i on ties) is committed. Unmasked positions: token -1, committed 0,
+ * conf 0; their logits rows are never read.
+ * Decisions are taken as in exact arithmetic evaluated in fp64: positions whose fast fp32
+ * estimate lies within a relative 1e-4 band of the threshold or of the fallback's best
+ * candidate are recomputed in fp64 on the device.
+ *
+ *   logits     [B, S, V]   dtype (finite values)   (device, read)
+ *   mask       [B, S]      uint8, nonzero = masked (device, read)
+ *   gamma      any non-NaN value (gamma <= 0 commits every masked position)
+ *   token_id   [B, S]      int32                   (device, written)
+ *   committed  [B, S]      uint8                   (device, written)
+ *   conf       [B, S]      float, may be NULL      (device, written)
+ *
+ * Supported: dtype TT_BF16 or TT_F32, 1 <= S <= 1024, 1 <= V, B*S*V < 2^40. B == 0 is a
+ * no-op.
+ * ------------------------------------------------------------------------------------- */
+size_t tt_commit_workspace(int32_t B, int32_t S, int32_t V, int32_t dtype);
+
+tt_status tt_commit(int32_t B, int32_t S, int32_t V, int32_t dtype, const void *logits,
+                    const uint8_t *mask, float gamma, int32_t *token_id, uint8_t *committed,
+                    float *conf, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Kernel timing (measurement support). While enabled, each call records HIP events on its
+ * stream around the kernels listed in tt_profile_stats. The events are created once, on
+ * the first enable (no device memory); up to 4096 calls per field are recorded, later ones
+ * are counted but not timed. tt_profile_read() synchronizes on the recorded events and
+ * returns the accumulated times; tt_profile_reset() clears them.
+ * ------------------------------------------------------------------------------------- */
+typedef struct {
+    int64_t attn_calls;       /* tt_block_denoise_attn calls timed                        */
+    double attn_total_ms;     /* sum over those calls, first launch to last              */
+    double attn_main_ms;      /* sum over those calls, the main attention kernel alone   */
+    int64_t commit_calls;     /* tt_commit calls timed                                   */
+    double commit_total_ms;   /* sum over those calls, first launch to last              */
+    double commit_reduce_ms;  /* sum over those calls, the vocabulary reduction kernel   */
+} tt_profile_stats;
+
+tt_status tt_profile_enable(int32_t enable);
+tt_status tt_profile_reset(void);
+tt_status tt_profile_read(tt_profile_stats *out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TT_H */

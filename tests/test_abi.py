@@ -1,0 +1,119 @@
+"""The C-ABI library loads and exports what include/tt.h declares; host-side validation
+returns the documented status codes without touching a GPU (CPU only)."""
+import ctypes
+
+import pytest
+
+import block_diffusion_lm_tt_amd as tt
+from block_diffusion_lm_tt_amd import _lib
+
+INVALID, UNSUPPORTED, WORKSPACE = 1, 2, 3
+
+
+def test_library_exports_every_declared_symbol():
+    L = tt.lib()
+    names = tt.header_symbols()
+    assert {"tt_block_denoise_attn", "tt_commit", "tt_block_denoise_attn_workspace", "tt_commit_workspace",
+            "tt_status_str", "tt_version", "tt_profile_enable", "tt_profile_reset", "tt_profile_read"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), f"libtt.so does not export {n}"
+
+
+def test_version_and_status_strings():
+    L = tt.lib()
+    assert L.tt_version() >> 16 == 1
+    for code, name in _lib.STATUS.items():
+        assert L.tt_status_str(code).decode() == name
+    assert L.tt_status_str(99).decode() == "TT_UNKNOWN_STATUS"
+
+
+def _shape(**kw):
+    d = dict(B=32, S=16, Hq=32, Hkv=2, D=128, Lmax=8192, dtype=_lib.TT_BF16)
+    d.update(kw)
+    return _lib.attn_shape(**{k: d[k] for k in ("B", "S", "Hq", "Hkv", "D", "Lmax")}, dtype_code=d["dtype"])
+
+
+def test_attn_workspace_query():
+    L = tt.lib()
+    ok = L.tt_block_denoise_attn_workspace(ctypes.byref(_shape()))
+    assert ok > 0 and ok % 256 == 0
+    assert L.tt_block_denoise_attn_workspace(ctypes.byref(_shape(dtype=_lib.TT_F32, D=64))) >= 256
+    assert L.tt_block_denoise_attn_workspace(ctypes.byref(_shape(Hq=30, Hkv=4))) == 0  # Hq % Hkv
+    assert L.tt_block_denoise_attn_workspace(ctypes.byref(_shape(D=512))) == 0
+    assert L.tt_block_denoise_attn_workspace(None) == 0
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation before any launch
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(S=0), INVALID), (dict(B=-1), INVALID), (dict(Hq=6, Hkv=4), INVALID), (dict(D=0), INVALID),
+    (dict(Lmax=-1), INVALID), (dict(dtype=7), UNSUPPORTED), (dict(D=300), UNSUPPORTED),
+    (dict(S=2048), UNSUPPORTED), (dict(B=20000), UNSUPPORTED),
+    (dict(B=4096, Lmax=65536), UNSUPPORTED),  # context storage past 2^31 elements
+])
+def test_attn_rejects_bad_shapes(kw, want):
+    L = tt.lib()
+    st = L.tt_block_denoise_attn(ctypes.byref(_shape(**kw)), *([FAKE] * 8), 1 << 30, None)
+    assert st == want
+
+
+def test_attn_rejects_null_pointers_and_short_workspace():
+    L = tt.lib()
+    sh = _shape()
+    need = L.tt_block_denoise_attn_workspace(ctypes.byref(sh))
+    for k in range(7):
+        ptrs = [FAKE] * 8
+        ptrs[k] = None
+        if k in (3, 4):  # k_ctx / v_ctx may only be NULL when Lmax == 0
+            assert L.tt_block_denoise_attn(ctypes.byref(sh), *ptrs, need, None) == INVALID
+        else:
+            assert L.tt_block_denoise_attn(ctypes.byref(sh), *ptrs, need, None) == INVALID
+    assert L.tt_block_denoise_attn(ctypes.byref(sh), *([FAKE] * 8), need - 1, None) == WORKSPACE
+    ptrs = [FAKE] * 7 + [None]
+    assert L.tt_block_denoise_attn(ctypes.byref(sh), *ptrs, need, None) == WORKSPACE
+    assert L.tt_block_denoise_attn(None, *([FAKE] * 8), need, None) == INVALID
+
+
+def test_attn_batch_zero_is_a_noop():
+    L = tt.lib()
+    assert L.tt_block_denoise_attn(ctypes.byref(_shape(B=0)), *([None] * 8), 0, None) == 0
+
+
+def test_commit_validation():
+    L = tt.lib()
+    need = L.tt_commit_workspace(32, 16, 131072, _lib.TT_BF16)
+    assert need > 0 and need % 256 == 0
+    assert L.tt_commit_workspace(1, 0, 10, 1) == 0
+    assert L.tt_commit_workspace(1, 2000, 10, 1) == 0
+    assert L.tt_commit_workspace(1, 2, 10, 5) == 0
+    args = lambda **kw: dict(dict(B=32, S=16, V=131072, dt=1, lg=FAKE, mk=FAKE, g=0.8, tok=FAKE, com=FAKE,  # noqa
+                                  conf=None, ws=FAKE, n=need), **kw)
+    call = lambda a: L.tt_commit(a["B"], a["S"], a["V"], a["dt"], a["lg"], a["mk"], a["g"], a["tok"],  # noqa
+                                 a["com"], a["conf"], a["ws"], a["n"], None)
+    assert call(args(g=float("nan"))) == INVALID
+    assert call(args(S=0)) == INVALID
+    assert call(args(V=0)) == INVALID
+    assert call(args(B=-2)) == INVALID
+    assert call(args(dt=3)) == UNSUPPORTED
+    assert call(args(S=1025)) == UNSUPPORTED
+    for k in ("lg", "mk", "tok", "com"):
+        assert call(args(**{k: None})) == INVALID
+    assert call(args(n=need - 1)) == WORKSPACE
+    assert call(args(ws=None)) == WORKSPACE
+    assert call(args(B=0, lg=None)) == 0
+
+
+def test_profile_api_without_gpu_work():
+    tt.profile_enable(True)
+    tt.profile_reset()
+    st = tt.profile_read()
+    assert st["attn_calls"] == 0 and st["commit_calls"] == 0
+    tt.profile_enable(False)
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 1, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        tt.tt_block_denoise_attn(q, q, q, q, q, torch.zeros(1, dtype=torch.int32))

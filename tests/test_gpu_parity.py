@@ -1,0 +1,249 @@
+"""GPU parity: the HIP path (through the C-ABI) against the fp64 CPU oracle on identical inputs.
+
+Bars: commit token_id / committed bit-exact; commit conf within 1e-5 relative; attention
+max-abs error <= 1e-4 for fp32 and <= 1e-2 for bf16 (outputs widened to fp64).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from block_diffusion_lm_tt_amd import tensors as TZ
+from block_diffusion_lm_tt_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL = {W.F32: 1e-4, W.BF16: 1e-2}
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_diffusion_lm_tt_amd as tt
+    tt.lib()  # the HIP library must be there: no fallback
+    return torch.device("cuda:0")
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _gpu_attn(x: W.AttnInputs, dev):
+    import block_diffusion_lm_tt_amd as tt
+    args = TZ.attn_to_device(x, dev)
+    out = tt.tt_block_denoise_attn(*args)
+    torch.cuda.synchronize()
+    return out.double().cpu().numpy()
+
+
+def _oracle_attn(x: W.AttnInputs):
+    from oracle import ttref_block_denoise_attn
+    return ttref_block_denoise_attn(x.B, x.S, x.Hq, x.Hkv, x.D, x.Lmax, x.dtype, x.q, x.k_blk, x.v_blk,
+                                    x.k_ctx, x.v_ctx, x.ctx_len)
+
+
+def _slice_b(x: W.AttnInputs, b: int, heads=None) -> W.AttnInputs:
+    """Sequence b alone (optionally one KV group's query heads), for sampled oracle checks."""
+    q, kb, vb, kc, vc = x.q[b:b + 1], x.k_blk[b:b + 1], x.v_blk[b:b + 1], x.k_ctx[b:b + 1], x.v_ctx[b:b + 1]
+    Hq, Hkv = x.Hq, x.Hkv
+    if heads is not None:  # (g, G): the G query heads of KV head g
+        g, G = heads
+        q = q[:, :, g * G:(g + 1) * G]
+        kb, vb, kc, vc = (t[:, :, g:g + 1] for t in (kb, vb, kc, vc))
+        Hq, Hkv = G, 1
+    c = np.ascontiguousarray
+    return W.AttnInputs(1, x.S, Hq, Hkv, x.D, x.Lmax, x.dtype, c(q), c(kb), c(vb), c(kc), c(vc),
+                        x.ctx_len[b:b + 1].copy())
+
+
+def _assert_attn(got, want, dtype, what):
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    err = np.abs(got - want).max()
+    _say(f"{what}: max-abs err {err:.3e}")
+    assert err <= TOL[dtype], f"{what}: max-abs error {err} > {TOL[dtype]}"
+
+
+# ------------------------------------------------------------------------------------------------
+# attention, whole outputs at oracle-friendly sizes (several tiles, ragged tails, split units)
+# ------------------------------------------------------------------------------------------------
+
+ATTN_CASES = [
+    # name, B, S, Hq, Hkv, D, ctx_lens, Lmax, dtype
+    ("mfma-ragged", 3, 16, 32, 2, 128, [0, 77, 300], 320, W.BF16),
+    ("mfma-tiny-rows", 2, 5, 6, 2, 128, [64, 129], 200, W.BF16),
+    ("mfma-S1", 4, 1, 16, 1, 128, [1, 63, 64, 65], 70, W.BF16),
+    ("mfma-S64-NQ8", 2, 64, 32, 2, 128, [500, 31], 512, W.BF16),
+    ("mfma-ctx0", 2, 16, 32, 2, 128, [0, 0], 0, W.BF16),
+    ("mfma-G1", 2, 16, 4, 4, 128, [130, 7], 130, W.BF16),
+    ("mfma-long-split", 1, 16, 32, 2, 128, [9000], 9000, W.BF16),
+    ("generic-f32-cfg1", 1, 16, 4, 1, 64, [128], 128, W.F32),
+    ("generic-bf16-D64", 2, 8, 8, 2, 64, [40, 300], 300, W.BF16),
+    ("generic-f32-D80", 2, 3, 6, 3, 80, [0, 257], 260, W.F32),
+]
+
+
+@pytest.mark.parametrize("case", ATTN_CASES, ids=[c[0] for c in ATTN_CASES])
+def test_attn_matches_oracle(dev, case):
+    name, B, S, Hq, Hkv, D, ctx, Lmax, dtype = case
+    _say(f"attn case {name}")
+    x = W.make_attn(B, S, Hq, Hkv, D, ctx, Lmax=Lmax, dtype=dtype, seed=100 + len(name))
+    _assert_attn(_gpu_attn(x, dev), _oracle_attn(x), dtype, name)
+
+
+def test_attn_padding_is_never_read(dev):
+    # NaN vs finite junk in the padding rows: bit-identical outputs
+    x = W.make_attn(3, 16, 32, 2, 128, [5, 200, 64], Lmax=256, dtype=W.BF16, seed=7)
+    a = _gpu_attn(x, dev)
+    y = W.AttnInputs(**{**x.__dict__})
+    y.k_ctx, y.v_ctx = x.k_ctx.copy(), x.v_ctx.copy()
+    for b in range(3):
+        y.k_ctx[b, x.ctx_len[b]:] = 0x4700
+        y.v_ctx[b, x.ctx_len[b]:] = 0xC700
+    assert np.array_equal(a, _gpu_attn(y, dev))
+
+
+def test_attn_block_permutation_equivariance(dev):
+    x = W.make_attn(2, 16, 32, 2, 128, [100, 3], Lmax=100, dtype=W.BF16, seed=9)
+    perm = np.random.default_rng(3).permutation(16)
+    y = W.AttnInputs(**{**x.__dict__})
+    y.q, y.k_blk, y.v_blk = (np.ascontiguousarray(t[:, perm]) for t in (x.q, x.k_blk, x.v_blk))
+    a, b = _gpu_attn(x, dev), _gpu_attn(y, dev)
+    assert np.abs(b - a[:, perm]).max() <= 1e-2
+
+
+def test_attn_deterministic_replay(dev):
+    x = W.WORKLOADS[3].attn(B=8)
+    assert np.array_equal(_gpu_attn(x, dev), _gpu_attn(x, dev))
+
+
+# ------------------------------------------------------------------------------------------------
+# attention at the workloads' full sizes: sampled sequences checked against the oracle
+# ------------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+def test_attn_workload_sampled(dev, cid):
+    w = W.WORKLOADS[cid]
+    _say(f"attn workload {cid}: {w.name}")
+    x = w.attn(step=1 if cid == 5 else 0, layer=2 if cid == 5 else 0)
+    got = _gpu_attn(x, dev)
+    if cid in (1, 2):
+        _assert_attn(got, _oracle_attn(x), x.dtype, f"workload {cid}")
+        return
+    if cid == 3:  # shortest, longest and two more sequences, all heads
+        order = np.argsort(x.ctx_len)
+        picks = sorted({int(order[0]), int(order[-1]), 5, 17})
+        for b in picks:
+            _assert_attn(got[b:b + 1], _oracle_attn(_slice_b(x, b)), x.dtype, f"workload 3 b={b}")
+        return
+    G = x.Hq // x.Hkv
+    picks = [(0, 0), (x.B - 1, x.Hkv - 1)]
+    for b, g in picks:
+        want = _oracle_attn(_slice_b(x, b, heads=(g, G)))
+        _assert_attn(got[b:b + 1, :, g * G:(g + 1) * G], want, x.dtype, f"workload {cid} b={b} g={g}")
+
+
+# ------------------------------------------------------------------------------------------------
+# commit
+# ------------------------------------------------------------------------------------------------
+
+def _gpu_commit(c: W.CommitInputs, dev, gamma=None):
+    import block_diffusion_lm_tt_amd as tt
+    lg, mk = TZ.commit_to_device(c, dev)
+    tok, com, conf = tt.tt_commit(lg, mk, c.gamma if gamma is None else gamma)
+    torch.cuda.synchronize()
+    return tok.cpu().numpy(), com.cpu().numpy(), conf.cpu().numpy()
+
+
+def _oracle_commit(c: W.CommitInputs, gamma=None):
+    from oracle import ttref_commit
+    return ttref_commit(c.B, c.S, c.V, c.dtype, c.logits, c.mask, c.gamma if gamma is None else gamma)
+
+
+def _assert_commit(c, dev, gamma=None, what=""):
+    g = c.gamma if gamma is None else gamma
+    tok, com, conf = _gpu_commit(c, dev, g)
+    otok, ocom, oconf, oz = _oracle_commit(c, g)
+    assert np.array_equal(tok, otok), f"{what}: token_id differs at {np.argwhere(tok != otok)[:5]}"
+    assert np.array_equal(com, ocom), f"{what}: committed differs at {np.argwhere(com != ocom)[:5]}"
+    m = c.mask.astype(bool)
+    np.testing.assert_allclose(conf[m], oconf[m], rtol=1e-5, atol=0)
+    assert np.all(conf[~m] == 0)
+    _say(f"{what}: gamma={g} committed {int(com.sum())} of {int(m.sum())} masked")
+    return com
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+def test_commit_workload(dev, cid):
+    w = W.WORKLOADS[cid]
+    c = w.commit(step=0)
+    gammas = [0.5, 0.8, 0.95] if cid == 5 else [c.gamma]
+    for g in gammas:
+        _assert_commit(c, dev, g, f"workload {cid}")
+
+
+@pytest.mark.parametrize("gamma", [0.0, -1.0, 1.0, 1.5, float("inf"), float("-inf"), 0.3])
+def test_commit_gamma_edges(dev, gamma):
+    c = W.make_commit(6, 16, 5000, W.BF16, seed=31, mask=W.random_mask(6, 16, 0, 16, seed=31),
+                      peaks={"mode": "bernoulli", "p": 0.5, "low": 2.0, "high": 12.0})
+    _assert_commit(c, dev, gamma, "edges")
+
+
+def test_commit_ties_and_duplicates(dev):
+    V = 4096
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((4, 8, V)).astype(np.float32) * 3
+    x[0, 0] = 1.25                    # all-equal row: token 0, conf 1/V
+    x[0, 1] = x[0, 2] = x[0, 3]       # duplicated rows: exact fallback tie -> lowest position
+    x[1, :, 7] = 40.0                 # max tie at 7 and 4000 -> token 7
+    x[1, :, 4000] = 40.0
+    x[2, :] = x[2, 0]                 # whole sequence identical rows
+    x[3, 5, 123] = 100.0              # one huge peak
+    bits = W.f32_to_bf16_bits(x)
+    mask = np.ones((4, 8), np.uint8)
+    mask[0, 0] = 0
+    for gamma in (0.8, 2.0, 0.0):
+        _assert_commit(W.CommitInputs(4, 8, V, W.BF16, bits, mask, gamma), dev, gamma, f"ties g={gamma}")
+    xf = np.ascontiguousarray(x)
+    _assert_commit(W.CommitInputs(4, 8, V, W.F32, xf, mask, 2.0), dev, 2.0, "ties f32")
+
+
+def test_commit_gamma_on_the_threshold(dev):
+    # gamma placed one float ulp below / at / above an exact confidence forces the fp64 recheck
+    c = W.make_commit(4, 16, 131072, W.BF16, seed=44, peaks={"mode": "bernoulli", "p": 0.8,
+                                                             "low": 13.0, "high": 18.0})
+    _, _, oconf, _ = _oracle_commit(c, 0.5)
+    target = float(np.sort(oconf.ravel())[-3])
+    for g in (np.nextafter(np.float32(target), np.float32(0)), np.float32(target),
+              np.nextafter(np.float32(target), np.float32(1))):
+        _assert_commit(c, dev, float(g), "threshold")
+
+
+@pytest.mark.parametrize("B,S,V,dtype", [
+    (3, 1, 1, W.BF16), (2, 7, 1001, W.BF16), (2, 7, 1001, W.F32), (1, 1000, 333, W.BF16),
+    (5, 16, 8193, W.BF16), (2, 16, 16383, W.F32), (0, 16, 100, W.BF16),
+])
+def test_commit_shapes(dev, B, S, V, dtype):
+    c = W.make_commit(B, S, V, dtype, seed=B * 1000 + S + V, mask=W.random_mask(B, S, 0, S, seed=V),
+                      peaks={"mode": "bernoulli", "p": 0.4, "low": 3.0, "high": 9.0})
+    if B == 0:
+        import block_diffusion_lm_tt_amd as tt
+        lg, mk = TZ.commit_to_device(c, dev)
+        tok, com, conf = tt.tt_commit(lg, mk, 0.5)
+        torch.cuda.synchronize()
+        assert tok.numel() == 0
+        return
+    for g in (0.05, 0.5, 1.2):
+        _assert_commit(c, dev, g, f"shape {B}x{S}x{V}")
+
+
+def test_commit_unmasked_rows_never_read(dev):
+    c = W.make_commit(2, 8, 2048, W.BF16, seed=3, mask=np.array([[1, 0] * 4, [0, 0, 0, 1, 0, 0, 0, 0]], np.uint8))
+    base = _gpu_commit(c, dev, 0.4)
+    junk = c.logits.copy()
+    junk[c.mask == 0] = 0x7FC0  # NaN in unmasked rows
+    d = W.CommitInputs(c.B, c.S, c.V, c.dtype, junk, c.mask, 0.4)
+    got = _gpu_commit(d, dev, 0.4)
+    for a, b in zip(base, got):
+        assert np.array_equal(a, b)
