@@ -1,0 +1,210 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-diffusion decoding step's hot path on one MI355X.
+
+One step = one pass of the hot path over one batch of the batched-serving workload
+(B=32 sequences, block S=16, Hq=32 query heads on Hkv=2 KV heads, head dim 128, context
+lengths U[1024,8192] in storage padded to 8192, bf16): the denoiser block attention over
+[context KV ; block KV] (tt_block_denoise_attn) followed by the gamma=0.8 confidence commit
+over logits[32,16,131072] (tt_commit). Inputs are seeded synthetic data resident in HBM
+before timing; the context KV and the logits rotate over several copies so that the
+256 MB last-level cache cannot serve them.
+
+Prints ONE JSON line on stdout. The metric is denoise-attention blocks per second (one
+block = one sequence's S-query block through one attention layer) together with the
+context-KV stream's achieved HBM bandwidth against the 8 TB/s peak.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "denoise-attn blocks/sec + context-KV HBM GB/s (% peak), S=16 ctx 8K bf16"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def attn_flops(x) -> float:
+    n = x.ctx_len.astype(np.int64) + x.S
+    return float(4 * x.S * x.Hq * x.D * int(n.sum()))
+
+
+def cpu_baseline(w, budget_s: float) -> dict:
+    """The fp64 oracle as it stands, on this host, on a bounded sample of the workload."""
+    from oracle import ttref_block_denoise_attn, ttref_threads
+    x = w.attn()
+    done, t_total, ctx_sum = 0, 0.0, 0
+    order = list(range(x.B))
+    for b in order:
+        xb = (x.q[b:b + 1], x.k_blk[b:b + 1], x.v_blk[b:b + 1], x.k_ctx[b:b + 1], x.v_ctx[b:b + 1],
+              x.ctx_len[b:b + 1].copy())
+        t0 = time.perf_counter()
+        ttref_block_denoise_attn(1, x.S, x.Hq, x.Hkv, x.D, x.Lmax, x.dtype, *xb)
+        t_total += time.perf_counter() - t0
+        done += 1
+        ctx_sum += int(x.ctx_len[b])
+        if t_total >= budget_s:
+            break
+    # scale: blocks/s over the sampled sequences, weighted to the full batch's mean context
+    full_mean = float(x.ctx_len.mean()) + x.S
+    samp_mean = ctx_sum / done + x.S
+    rate = done / t_total * (samp_mean / full_mean)
+    return {"value": rate, "unit": "blocks/s", "cores": ttref_threads(), "kind": "oracle",
+            "sample": f"{done} of {x.B} sequences of the timed workload (sum ctx_len {ctx_sum}), "
+                      f"{t_total:.1f} s, rate rescaled to the batch's mean context length"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=3, help="workload id; the headline line is 3")
+    ap.add_argument("--rotate", type=int, default=4, help="copies of context KV / logits cycled")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work sampled")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the hot path has no multi-GPU collective and this build does not run on more than one "
+              "GPU.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import block_diffusion_lm_tt_amd as tt
+    from block_diffusion_lm_tt_amd import tensors as TZ
+    from block_diffusion_lm_tt_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    tt.lib()
+    w = W.WORKLOADS[args.config]
+    if w.layers != 1:
+        print("bench.py times a single-layer workload (1-4); the block loop is bench_loop.py",
+              file=sys.stderr)
+        sys.exit(2)
+
+    log(f"[bench] generating workload {w.cid}: {w.name}")
+    x = w.attn()
+    c = w.commit()
+    q, kb, vb, kc, vc, ctx = TZ.attn_to_device(x, dev)
+    lg, mk = TZ.commit_to_device(c, dev)
+    R = max(1, args.rotate)
+    kcs = [kc] + [kc.clone() for _ in range(R - 1)]
+    vcs = [vc] + [vc.clone() for _ in range(R - 1)]
+    lgs = [lg] + [lg.clone() for _ in range(R - 1)]
+    out = torch.empty_like(q)
+    ws_a = torch.empty(max(1, tt.tt_block_denoise_attn_workspace(x.B, x.S, x.Hq, x.Hkv, x.D, x.Lmax,
+                                                                 1 if x.dtype == W.BF16 else 0)),
+                       dtype=torch.uint8, device=dev)
+    ws_c = torch.empty(max(1, tt.tt_commit_workspace(c.B, c.S, c.V, 1 if c.dtype == W.BF16 else 0)),
+                       dtype=torch.uint8, device=dev)
+    tok = torch.empty((c.B, c.S), dtype=torch.int32, device=dev)
+    com = torch.empty((c.B, c.S), dtype=torch.uint8, device=dev)
+    conf = torch.empty((c.B, c.S), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step(k: int):
+        r = k % R
+        tt.tt_block_denoise_attn(q, kb, vb, kcs[r], vcs[r], ctx, out=out, workspace=ws_a)
+        tt.tt_commit(lgs[r], mk, c.gamma, token_id=tok, committed=com, conf=conf, workspace=ws_c)
+
+    log(f"[bench] warmup {args.warmup}")
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    tt.profile_enable(True)
+    tt.profile_reset()
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(k)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    prof = tt.profile_read()
+    tt.profile_enable(False)
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: {args.copy_probe_mib} MiB device-to-device copy x3")
+
+    K = args.steps
+    t_attn = prof["attn_total_ms"] / max(1, prof["attn_calls"]) * 1e-3
+    t_main = prof["attn_main_ms"] / max(1, prof["attn_calls"]) * 1e-3
+    t_commit = prof["commit_total_ms"] / max(1, prof["commit_calls"]) * 1e-3
+    t_reduce = prof["commit_reduce_ms"] / max(1, prof["commit_calls"]) * 1e-3
+    kv_bytes = x.ctx_kv_bytes
+    blocks_per_s = x.B / t_attn
+    gbs_call = kv_bytes / t_attn / 1e9
+    gbs_main = kv_bytes / t_main / 1e9
+    tflops = attn_flops(x) / t_main / 1e12
+    commit_bytes = c.masked_row_bytes
+    log(f"[bench] attn {t_attn*1e6:.1f} us/call (main kernel {t_main*1e6:.1f} us), "
+        f"commit {t_commit*1e6:.1f} us/call (reduce {t_reduce*1e6:.1f} us), step {wall/K*1e3:.3f} ms")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline (oracle), budget {args.cpu_budget} s")
+        cpu = cpu_baseline(w, args.cpu_budget)
+        log(f"[bench] cpu baseline {cpu['value']:.3f} blocks/s on {cpu['cores']} threads")
+
+    res = {
+        "metric": METRIC,
+        "value": blocks_per_s,
+        "unit": "blocks/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": wall / K * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if x.dtype == W.BF16 else "f32",
+        "data": "synthetic (seeded; N(0,1) Q/K/V, N(0,3) logits with planted peaks)",
+        "config": {"workload": w.name, "B": x.B, "S": x.S, "Hq": x.Hq, "Hkv": x.Hkv, "D": x.D,
+                   "Lmax": x.Lmax, "sum_ctx_len": int(x.ctx_len.sum()), "V": c.V, "gamma": c.gamma,
+                   "masked_positions": int(c.mask.sum()), "rotated_copies": R},
+        "context_kv_GBps": gbs_call,
+        "context_kv_pct_hbm_peak": 100.0 * gbs_call / HBM_PEAK_GBS,
+        "attn_us_per_call": t_attn * 1e6,
+        "commit_us_per_call": t_commit * 1e6,
+        "commit_GBps": commit_bytes / t_commit / 1e9,
+        "mfma_TFLOPs": tflops,
+        "mfma_pct_bf16_peak": 100.0 * tflops / MFMA_BF16_PEAK_TFLOPS,
+        "roofline": {"kernel": "attn_mfma_kernel", "bound": "hbm", "achieved": gbs_main,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs_main / HBM_PEAK_GBS,
+                     "traffic": None, "avg_us": t_main * 1e6,
+                     "algorithmic_bytes_per_launch": kv_bytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

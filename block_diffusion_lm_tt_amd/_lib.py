@@ -14,7 +14,7 @@ import re
 from typing import Optional, Tuple
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libtt.so")
+LIB_PATH = os.environ.get("TT_LIB", os.path.join(HERE, "libtt.so"))  # TT_LIB: another build of libtt
 HEADER = os.path.join(os.path.dirname(HERE), "include", "tt.h")
 
 TT_F32, TT_BF16 = 0, 1

@@ -6,28 +6,31 @@
 // Z = sum_v exp(l_v - max), conf = 1/Z, committed = conf > gamma; a sequence with masked
 // positions and no commit commits its most confident masked position (lowest i on ties).
 //
-// How: the work is one pass over the masked rows' logits, so it is HBM bound.
-//  1. commit_reduce: one workgroup per (masked row, 8192-element vocabulary chunk). Each
-//     thread loads its 32 (bf16) or 16 (fp32) elements with 16-byte loads, keeps them in
-//     registers, finds its max and lowest argmax, and the workgroup merges them (wave
-//     shuffles + LDS, lowest index on ties). A second pass over the registers sums
-//     exp2((x - max) * log2 e) in fp32 per thread and in fp64 across threads.
-//  2. commit_merge: one workgroup per sequence merges the chunks in fp64, estimates Z and
-//     takes every decision whose margin is safe. The estimate's relative error is below
-//     1e-5 (fp32 exp2 of an exactly formed difference, <= 32 terms per fp32 partial), so a
-//     decision is taken only outside a relative band of 1e-4 around the threshold, and
-//     fallback candidates are all positions within 4e-4 of the best estimate. Positions in
-//     a band are flagged.
-//  3. commit_recheck: flagged rows only -- Z recomputed over the full row with fp64 exp.
-//  4. commit_finalize: sequences with flagged rows decide with the fp64 values (conf =
-//     1/Z > gamma, evaluated in fp64 as in exact arithmetic) and apply the fallback.
+// How: the work is one pass over the masked rows' logits, so it is HBM bound. Two
+// launches, with no communication between workgroups inside a launch:
+//  1. commit_reduce: one workgroup per (masked row, vocabulary chunk). Each thread loads its
+//     chunk elements with 16-byte non-temporal loads into registers, finds its max and
+//     lowest argmax, and the workgroup merges them (wave shuffles + LDS, lowest index on
+//     ties); a second pass over the registers sums exp2((x - max) * log2 e) in fp32 per
+//     thread and fp64 across threads. Unmasked rows exit at once and are never read.
+//  2. commit_decide: one workgroup per sequence. It merges each masked row's chunks in chunk
+//     order (fp64), giving the row's token and an estimate of Z whose relative error is
+//     below 1e-5 (exp2 of an exactly formed difference, <= 64 terms per fp32 partial). A
+//     threshold decision is taken on the estimate only outside a relative band of 1e-4; the
+//     fallback is taken on the estimate only when its winner leads every other position by
+//     more than 4e-4. Positions inside a band are recomputed by the same workgroup over the
+//     full row with fp64 exp and decided on those values (conf = 1/Z > gamma, in fp64 as in
+//     exact arithmetic), so every integer output is the exact-arithmetic decision except
+//     for margins below fp64 rounding.
 #include "tt_internal.h"
 
 namespace tt {
 namespace {
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int NT = 256;
-constexpr int LOADS = 4;  // 16-byte loads per thread per chunk
+constexpr int LOADS = 8;  // 16-byte loads per thread per chunk
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr double kBand = 1e-4;       // threshold band (relative)
 constexpr double kFallBand = 4e-4;   // fallback candidate band (relative)
@@ -69,7 +72,7 @@ __global__ __launch_bounds__(NT) void commit_reduce_kernel(CommitArgs a) {
     const int i0 = begin + (ld * NT + tid) * VE;
     const T* p = base + i0;
     if (i0 + VE <= end && ((reinterpret_cast<uintptr_t>(p) & 15) == 0)) {
-      const uint4 v = *reinterpret_cast<const uint4*>(p);
+      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
       const T* e = reinterpret_cast<const T*>(&v);
 #pragma unroll
       for (int k = 0; k < VE; ++k) x[ld * VE + k] = to_f(e[k]);
@@ -107,7 +110,7 @@ __global__ __launch_bounds__(NT) void commit_reduce_kernel(CommitArgs a) {
 
   float zf = 0.0f;
 #pragma unroll
-  for (int i = 0; i < EPT; ++i) zf += exp2f((x[i] - M) * kLog2e);  // -inf -> 0
+  for (int i = 0; i < EPT; ++i) zf += __builtin_amdgcn_exp2f((x[i] - M) * kLog2e);  // -inf -> 0
   double z = (double)zf;
   for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off, 64);
   if (lane == 0) sm_z[w] = z;
@@ -121,124 +124,198 @@ __global__ __launch_bounds__(NT) void commit_reduce_kernel(CommitArgs a) {
   }
 }
 
-// Workgroup-wide helpers for the per-sequence kernels (blockDim.x = multiple of 64, <= 1024).
-__device__ __forceinline__ double block_min_d(double v, double* red) {
-  for (int off = 32; off > 0; off >>= 1) v = fmin(v, __shfl_xor(v, off, 64));
-  const int nw = blockDim.x >> 6;
+// ---- per-sequence decision -----------------------------------------------------------
+
+constexpr int DT = 512;            // threads of the decision workgroup
+constexpr int DW = DT / 64;
+constexpr int MAXP = 1024 / DT;    // positions per thread (S <= 1024)
+
+__device__ __forceinline__ double dblock_max(double v, double* red) {
+  for (int off = 32; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off, 64));
+  __syncthreads();
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
   double r = red[0];
-  for (int k = 1; k < nw; ++k) r = fmin(r, red[k]);
-  __syncthreads();
+  for (int k = 1; k < DW; ++k) r = fmax(r, red[k]);
   return r;
 }
 
-__global__ void commit_merge_kernel(CommitArgs a) {
-  __shared__ double red[16];
-  const int b = blockIdx.x, i = threadIdx.x;
-  const bool in = i < a.S;
-  const size_t row = (size_t)b * a.S + i;
-  const bool masked = in && a.mask[row];
-  float M = -INFINITY;
-  int tok = 0x7fffffff;
-  double Z = INFINITY;
-  bool sure = false, band = false;
-  if (masked) {
-    const CommitChunk* c = a.chunks + row * a.n_chunks;
-    for (int k = 0; k < a.n_chunks; ++k) argmax_merge(M, tok, c[k].m, c[k].tok);
-    Z = 0.0;
-    for (int k = 0; k < a.n_chunks; ++k) Z += c[k].z * exp((double)c[k].m - (double)M);
-    const double zg = Z * (double)a.gamma;
-    band = fabs(zg - 1.0) <= kBand;
-    sure = !band && zg < 1.0;
-  }
-  const bool any_sure = __syncthreads_or(sure);
-  const bool any_masked = __syncthreads_or(masked);
-  bool cand = false;
-  if (!any_sure && any_masked) {
-    const double zmin = block_min_d(masked ? Z : INFINITY, red);
-    cand = masked && Z <= zmin * (1.0 + kFallBand);
-  }
-  const bool flag = band || cand;
-  const bool any_flag = __syncthreads_or(flag);
-  if (in) {
-    CommitRow r;
-    r.m = M;
-    r.tok = tok;
-    r.z_est = Z;
-    r.z_exact = 0.0;
-    r.flag = flag ? 1 : 0;
-    r.decided = sure ? 1 : 0;
-    a.rows[row] = r;
-  }
-  if (!any_flag) {
-    // every decision is safe; with no sure commit there would have been a flagged candidate
-    if (in) {
-      a.token_id[row] = masked ? tok : -1;
-      a.committed[row] = sure ? 1 : 0;
-      if (a.conf) a.conf[row] = masked ? (float)(1.0 / Z) : 0.0f;
-    }
-    if (i == 0) a.seq_done[b] = 1;
-  } else if (i == 0) {
-    a.seq_done[b] = 0;
-  }
+__device__ __forceinline__ double dblock_sum(double v, double* red) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  double r = red[0];
+  for (int k = 1; k < DW; ++k) r += red[k];
+  return r;
+}
+
+__device__ __forceinline__ int iblock_min(int v, int* red) {
+  for (int off = 32; off > 0; off >>= 1) v = min(v, __shfl_xor(v, off, 64));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int r = red[0];
+  for (int k = 1; k < DW; ++k) r = min(r, red[k]);
+  return r;
+}
+
+__device__ __forceinline__ int iblock_sum(int v, int* red) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int r = red[0];
+  for (int k = 1; k < DW; ++k) r += red[k];
+  return r;
+}
+
+// fp64 Z of one row, by the whole workgroup (fixed reduction order: deterministic)
+template <typename T>
+__device__ double row_z_fp64(const T* row, int V, double M, double* red) {
+  double z = 0.0;
+  for (int v = threadIdx.x; v < V; v += DT) z += exp((double)to_f(row[v]) - M);
+  return dblock_sum(z, red);
 }
 
 template <typename T>
-__global__ __launch_bounds__(NT) void commit_recheck_kernel(CommitArgs a) {
-  __shared__ double red[4];
-  const size_t row = blockIdx.x;
-  const int b = (int)(row / a.S);
-  if (a.seq_done[b] || !a.mask[row] || !a.rows[row].flag) return;
-  const T* base = static_cast<const T*>(a.logits) + row * a.V;
-  const double M = (double)a.rows[row].m;
-  double z = 0.0;
-  for (int v = threadIdx.x; v < a.V; v += NT) z += exp((double)to_f(base[v]) - M);
-  for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off, 64);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = z;
-  __syncthreads();
-  if (threadIdx.x == 0) a.rows[row].z_exact = (red[0] + red[1]) + (red[2] + red[3]);
-}
-
-__global__ void commit_finalize_kernel(CommitArgs a) {
-  __shared__ double red[16];
-  const int b = blockIdx.x, i = threadIdx.x;
-  if (a.seq_done[b]) return;
-  const bool in = i < a.S;
-  const size_t row = (size_t)b * a.S + i;
-  const bool masked = in && a.mask[row];
-  double conf = -1.0;
-  bool c = false;
-  int tok = -1;
-  if (masked) {
-    const CommitRow r = a.rows[row];
-    tok = r.tok;
-    if (r.flag) {
-      conf = 1.0 / r.z_exact;
-      c = conf > (double)a.gamma;
+__global__ __launch_bounds__(DT) void commit_decide_kernel(CommitArgs a) {
+  __shared__ double redd[DW];
+  __shared__ int redi[DW];
+  __shared__ int flagged_list[1024];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const T* logits = static_cast<const T*>(a.logits);
+  bool msk[MAXP];
+  float mm[MAXP];
+  double zz[MAXP];
+  int tk[MAXP], fl[MAXP], dec[MAXP];
+  int any_c = 0, nflag = 0, nmask = 0;
+#pragma unroll
+  for (int p = 0; p < MAXP; ++p) {
+    const int i = tid + p * DT;
+    const size_t row = (size_t)b * a.S + i;
+    msk[p] = i < a.S && a.mask[row];
+    mm[p] = -INFINITY;
+    zz[p] = 1.0;
+    tk[p] = -1;
+    fl[p] = dec[p] = 0;
+    if (i < a.S && !msk[p]) {
+      a.token_id[row] = -1;
+      a.committed[row] = 0;
+      if (a.conf) a.conf[row] = 0.0f;
+    }
+    if (!msk[p]) continue;
+    ++nmask;
+    // merge the row's chunks in chunk order
+    const CommitChunk* c = a.chunks + row * a.n_chunks;
+    float M = -INFINITY;
+    int tok = 0x7fffffff;
+#pragma unroll 8
+    for (int k = 0; k < a.n_chunks; ++k) argmax_merge(M, tok, c[k].m, c[k].tok);
+    double Z = 0.0;
+#pragma unroll 8
+    for (int k = 0; k < a.n_chunks; ++k) Z += c[k].z * exp((double)c[k].m - (double)M);
+    mm[p] = M;
+    tk[p] = tok;
+    zz[p] = Z;
+    const double zg = Z * (double)a.gamma;
+    if (fabs(zg - 1.0) <= kBand) {
+      fl[p] = 1;
+      ++nflag;
     } else {
-      conf = 1.0 / r.z_est;
-      c = r.decided != 0;
+      dec[p] = zg < 1.0;
+    }
+    any_c |= dec[p];
+  }
+  any_c = __syncthreads_or(any_c);
+  nmask = iblock_sum(nmask, redi);
+  int nflag_tot = iblock_sum(nflag, redi);
+  // fallback on the estimates when it is unambiguous; otherwise flag every candidate
+  bool fallback_pending = false;
+  if (!any_c && nmask > 0) {
+    double my = -1.0;
+#pragma unroll
+    for (int p = 0; p < MAXP; ++p)
+      if (msk[p]) my = fmax(my, 1.0 / zz[p]);
+    const double best = dblock_max(my, redd);
+    int mi = 0x7fffffff;
+#pragma unroll
+    for (int p = 0; p < MAXP; ++p)
+      if (msk[p] && 1.0 / zz[p] == best) mi = min(mi, tid + p * DT);
+    const int bi = iblock_min(mi, redi);
+    double my2 = -1.0;
+#pragma unroll
+    for (int p = 0; p < MAXP; ++p)
+      if (msk[p] && tid + p * DT != bi) my2 = fmax(my2, 1.0 / zz[p]);
+    const double second = dblock_max(my2, redd);
+    if (nflag_tot > 0 || (second >= 0.0 && best <= second * (1.0 + kFallBand))) {
+      fallback_pending = true;
+#pragma unroll
+      for (int p = 0; p < MAXP; ++p)
+        if (msk[p] && fl[p] == 0 && (1.0 / zz[p]) * (1.0 + kFallBand) >= best) {
+          fl[p] = 1;
+          ++nflag;
+        }
+      nflag_tot = iblock_sum(nflag, redi);
+    } else {
+#pragma unroll
+      for (int p = 0; p < MAXP; ++p)
+        if (tid + p * DT == bi) dec[p] = 1;
     }
   }
-  const bool any_c = __syncthreads_or(c);
-  const bool any_masked = __syncthreads_or(masked);
-  if (!any_c && any_masked) {
-    // most confident masked position, lowest i on ties: minimise (-conf, i)
-    const double best = -block_min_d(masked ? -conf : INFINITY, red);
-    const bool at_best = masked && conf == best;
-    // lowest i attaining the best value
-    __shared__ int first;
-    if (i == 0) first = 0x7fffffff;
+  if (nflag_tot > 0) {
+    // fp64 recomputation of every flagged row by the whole workgroup
+    __shared__ int nl;
+    if (tid == 0) nl = 0;
     __syncthreads();
-    if (at_best) atomicMin(&first, i);
+#pragma unroll
+    for (int p = 0; p < MAXP; ++p)
+      if (fl[p]) flagged_list[atomicAdd(&nl, 1)] = tid + p * DT;
     __syncthreads();
-    c = (i == first);
+    const int n = nl;
+    for (int f = 0; f < n; ++f) {
+      const int i = flagged_list[f];
+      const size_t row = (size_t)b * a.S + i;
+      __shared__ float Mf;
+      if ((i % DT) == tid) Mf = mm[i / DT];
+      __syncthreads();
+      const double z = row_z_fp64(logits + row * a.V, a.V, (double)Mf, redd);
+      if ((i % DT) == tid) zz[i / DT] = z;
+      __syncthreads();
+    }
+    any_c = 0;
+#pragma unroll
+    for (int p = 0; p < MAXP; ++p) {
+      if (!msk[p]) continue;
+      if (fl[p]) dec[p] = (1.0 / zz[p]) > (double)a.gamma;  // band rows decided exactly
+      any_c |= dec[p];
+    }
+    any_c = __syncthreads_or(any_c);
+    if (!any_c && (fallback_pending || nmask > 0)) {
+      // most confident masked position (flagged rows carry exact values; every other row
+      // is outside the candidate band), lowest position on ties
+      double my = -1.0;
+#pragma unroll
+      for (int p = 0; p < MAXP; ++p)
+        if (msk[p]) my = fmax(my, 1.0 / zz[p]);
+      const double best = dblock_max(my, redd);
+      int mi = 0x7fffffff;
+#pragma unroll
+      for (int p = 0; p < MAXP; ++p)
+        if (msk[p] && 1.0 / zz[p] == best) mi = min(mi, tid + p * DT);
+      const int bi = iblock_min(mi, redi);
+#pragma unroll
+      for (int p = 0; p < MAXP; ++p)
+        if (tid + p * DT == bi) dec[p] = 1;
+    }
   }
-  if (in) {
-    a.token_id[row] = masked ? tok : -1;
-    a.committed[row] = c ? 1 : 0;
-    if (a.conf) a.conf[row] = masked ? (float)conf : 0.0f;
+#pragma unroll
+  for (int p = 0; p < MAXP; ++p) {
+    if (!msk[p]) continue;
+    const size_t row = (size_t)b * a.S + tid + p * DT;
+    a.token_id[row] = tk[p];
+    a.committed[row] = dec[p] ? 1 : 0;
+    if (a.conf) a.conf[row] = (float)(1.0 / zz[p]);
   }
 }
 
@@ -248,7 +325,6 @@ int commit_chunk_elems(int dtype) { return NT * LOADS * (dtype == TT_BF16 ? 8 : 
 
 hipError_t launch_commit(const CommitArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   const long long nblk = (long long)a.B * a.S * a.n_chunks;
-  const int seq_threads = ((a.S + 63) / 64) * 64;
   if (ev0) (void)hipEventRecord(ev0, s);
   if (a.dtype == TT_BF16)
     hipLaunchKernelGGL(commit_reduce_kernel<uint16_t>, dim3((unsigned)nblk), dim3(NT), 0, s, a);
@@ -257,14 +333,10 @@ hipError_t launch_commit(const CommitArgs& a, hipStream_t s, hipEvent_t ev0, hip
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (ev1) (void)hipEventRecord(ev1, s);
-  hipLaunchKernelGGL(commit_merge_kernel, dim3(a.B), dim3(seq_threads), 0, s, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.dtype == TT_BF16)
-    hipLaunchKernelGGL(commit_recheck_kernel<uint16_t>, dim3(a.B * a.S), dim3(NT), 0, s, a);
+    hipLaunchKernelGGL(commit_decide_kernel<uint16_t>, dim3(a.B), dim3(DT), 0, s, a);
   else
-    hipLaunchKernelGGL(commit_recheck_kernel<float>, dim3(a.B * a.S), dim3(NT), 0, s, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(commit_finalize_kernel, dim3(a.B), dim3(seq_threads), 0, s, a);
+    hipLaunchKernelGGL(commit_decide_kernel<float>, dim3(a.B), dim3(DT), 0, s, a);
   return hipGetLastError();
 }
 

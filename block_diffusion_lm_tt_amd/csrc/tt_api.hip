@@ -39,7 +39,7 @@ tt_status plan_attn(const tt_attn_shape* sh, AttnPlan* p) {
   p->NC = nc < 8 ? 8 : nc;
   if (p->mfma) {
     p->plan_bytes = align_up((size_t)(sh->B + 1) * sizeof(int32_t));
-    p->part_bytes = align_up((size_t)p->NC * 2 * p->NQ * kAttnRowsPerWg * (kAttnMfmaD + 2) * sizeof(float));
+    p->part_bytes = align_up(attn_part_bytes(p->NC, p->NQ));
   } else {
     p->plan_bytes = p->part_bytes = 0;
   }
@@ -48,7 +48,7 @@ tt_status plan_attn(const tt_attn_shape* sh, AttnPlan* p) {
 
 struct CommitPlan {
   int n_chunks, chunk_elems;
-  size_t chunk_bytes, row_bytes, done_bytes;
+  size_t chunk_bytes;
 };
 
 tt_status plan_commit(int32_t B, int32_t S, int32_t V, int32_t dtype, CommitPlan* p) {
@@ -59,8 +59,7 @@ tt_status plan_commit(int32_t B, int32_t S, int32_t V, int32_t dtype, CommitPlan
   p->chunk_elems = commit_chunk_elems(dtype);
   p->n_chunks = (V + p->chunk_elems - 1) / p->chunk_elems;
   p->chunk_bytes = align_up((size_t)B * S * p->n_chunks * sizeof(CommitChunk));
-  p->row_bytes = align_up((size_t)B * S * sizeof(CommitRow));
-  p->done_bytes = align_up((size_t)B * sizeof(int32_t));
+
   return TT_OK;
 }
 
@@ -175,7 +174,7 @@ tt_status tt_block_denoise_attn(const tt_attn_shape* shape, const void* q, const
 size_t tt_commit_workspace(int32_t B, int32_t S, int32_t V, int32_t dtype) {
   CommitPlan p;
   if (plan_commit(B, S, V, dtype, &p) != TT_OK) return 0;
-  const size_t n = p.chunk_bytes + p.row_bytes + p.done_bytes;
+  const size_t n = p.chunk_bytes;
   return n < kAlign ? kAlign : n;
 }
 
@@ -200,8 +199,6 @@ tt_status tt_commit(int32_t B, int32_t S, int32_t V, int32_t dtype, const void* 
   a.conf = conf;
   char* ws = static_cast<char*>(workspace);
   a.chunks = reinterpret_cast<CommitChunk*>(ws);
-  a.rows = reinterpret_cast<CommitRow*>(ws + p.chunk_bytes);
-  a.seq_done = reinterpret_cast<int32_t*>(ws + p.chunk_bytes + p.row_bytes);
   a.B = B;
   a.S = S;
   a.V = V;

@@ -6,7 +6,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/tt.h"
+#include "tt.h"
 
 namespace tt {
 
@@ -14,12 +14,12 @@ namespace tt {
 // attention
 // ---------------------------------------------------------------------------------------
 
-constexpr int kAttnKeysPerTile = 64;   // keys staged in LDS per pipeline step
+constexpr int kAttnKeysPerTile = 32;   // keys staged in LDS per pipeline step
 constexpr int kAttnWaves = 4;          // waves per workgroup of the MFMA kernel
-constexpr int kAttnRowsPerWave = 32;   // query rows (head-in-group x block position) per wave
+constexpr int kAttnRowsPerWave = 64;   // query rows (head-in-group x block position) per wave
 constexpr int kAttnRowsPerWg = kAttnWaves * kAttnRowsPerWave;
 constexpr int kAttnMfmaD = 128;        // head dim of the MFMA kernel
-constexpr int kMaxB = 16383;           // largest batch (the tile plan sits in LDS)
+constexpr int kMaxB = 8191;            // largest batch (the tile plan sits in LDS)
 
 struct AttnArgs {
   const void* q;
@@ -29,7 +29,7 @@ struct AttnArgs {
   const void* v_ctx;
   const int32_t* ctx_len;
   void* o;
-  float* part;        // partial results: [n_clusters*2][NQ][rows_wg*(D+2)] fp32
+  float* part;        // partial results per (cluster, segment, query slice)
   int32_t* plan;      // [B+1] tile prefix sums, written by workgroup 0 for the combine
   int B, S, Hq, Hkv, G, D, Lmax;
   int NQ;             // workgroups (query slices) per (sequence, KV head) unit
@@ -39,6 +39,7 @@ struct AttnArgs {
 
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s, hipEvent_t ev_main0, hipEvent_t ev_main1);
 hipError_t launch_attn_generic(const AttnArgs& a, int dtype, hipStream_t s);
+size_t attn_part_bytes(int nc, int nq);  // partial-result workspace of the MFMA path
 
 // ---------------------------------------------------------------------------------------
 // commit
@@ -50,15 +51,6 @@ struct CommitChunk {   // per (row, vocabulary chunk): partial max / argmax / su
   double z;
 };
 
-struct CommitRow {     // per (b, i): merged values and the decision state
-  float m;
-  int32_t tok;
-  double z_est;        // fast estimate
-  double z_exact;      // fp64 recomputation (valid when flag != 0)
-  int32_t flag;        // 1 = recompute in fp64
-  int32_t decided;     // 1 = committed by a sure threshold decision
-};
-
 struct CommitArgs {
   const void* logits;
   const uint8_t* mask;
@@ -66,9 +58,7 @@ struct CommitArgs {
   int32_t* token_id;
   uint8_t* committed;
   float* conf;
-  CommitChunk* chunks;  // [B*S][n_chunks]
-  CommitRow* rows;      // [B*S]
-  int32_t* seq_done;    // [B]
+  CommitChunk* chunks;     // [B*S][n_chunks]
   int B, S, V;
   int n_chunks, chunk_elems;
   int dtype;

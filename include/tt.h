@@ -85,7 +85,7 @@ const char *tt_status_str(tt_status s);
  * into [0, Lmax] before use (a value outside that range is a caller error, not a fault).
  *
  * Supported: dtype TT_BF16 or TT_F32; 1 <= D <= 256 (D == 128 with bf16 takes the MFMA
- * path); 1 <= S <= 1024; B*S*Hq*D, B*Lmax*Hkv*D < 2^31; B <= 16383. Anything else returns
+ * path); 1 <= S <= 1024; B*S*Hq*D, B*Lmax*Hkv*D < 2^31; B <= 8191. Anything else returns
  * TT_ERR_UNSUPPORTED. B == 0 is a no-op. k_ctx/v_ctx may be NULL only when Lmax == 0.
  * ------------------------------------------------------------------------------------- */
 size_t tt_block_denoise_attn_workspace(const tt_attn_shape *shape);

@@ -34,6 +34,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define TTREF_F32 0
 #define TTREF_BF16 1
@@ -51,6 +54,16 @@ static double ttref_load(const void *base, size_t idx, int dtype)
     float f;
     memcpy(&f, &bits, sizeof f);
     return (double)f;
+}
+
+/* Number of host threads the oracle's parallel loops use (reported with its timings). */
+int ttref_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
 }
 
 /* Exported so that the tests can pin the decode itself against a library conversion. */

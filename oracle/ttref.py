@@ -35,6 +35,8 @@ def _lib():
         L.ttref_commit.restype = i32
         L.ttref_decode.argtypes = [vp, ctypes.c_size_t, i32]
         L.ttref_decode.restype = ctypes.c_double
+        L.ttref_threads.argtypes = []
+        L.ttref_threads.restype = i32
         _LIB = L
     return _LIB
 
@@ -47,6 +49,11 @@ def _check_dtype(a: np.ndarray, dtype: str):
     want = np.uint16 if dtype == "bf16" else np.float32
     if a.dtype != want or not a.flags.c_contiguous:
         raise TypeError(f"expected contiguous {want} array for dtype {dtype}, got {a.dtype}")
+
+
+def ttref_threads() -> int:
+    """Host threads used by the oracle's parallel loops."""
+    return int(_lib().ttref_threads())
 
 
 def ttref_decode(a: np.ndarray, dtype: str) -> np.ndarray:
