@@ -9,10 +9,9 @@
 // How (MI355X design):
 //  * A unit is one (sequence b, KV head g). All G*S query rows of a unit read the same
 //    keys, so they are packed as the N side of the MFMAs: S^T = K Q^T and O^T += V^T P^T
-//    with v_mfma_f32_32x32x16_bf16. Each of the 4 waves of a workgroup owns 64 query rows
-//    (two 32-column MFMA blocks, so every K/V operand read from LDS feeds two products);
-//    256 rows per workgroup, one workgroup per CU. A unit with more rows is covered by NQ
-//    workgroups (a "cluster") placed on one XCD so that its key stream is fetched from
+//    with v_mfma_f32_32x32x16_bf16. A workgroup of 8 waves covers 256 query rows, 32 per
+//    wave; one workgroup per CU, two waves per SIMD. A unit with more rows is covered by
+//    NQ workgroups (a "cluster") placed on one XCD so that its key stream is fetched from
 //    HBM once and shared through that XCD's L2.
 //  * Keys of a unit are the concatenation [context ; block]; the key sequence is cut in
 //    32-key tiles. All tiles of all units form one global list that is split evenly over
@@ -21,10 +20,9 @@
 //    range boundary leaves per-piece partials (running max and sum in fp32, normalised O
 //    in bf16) that the combine kernel merges with a log-sum-exp rescale.
 //  * K and V tiles go HBM -> LDS directly (global_load_lds_dwordx4, no staging registers)
-//    into a ring of 8 stages of 16 KB (8 KB of keys + 8 KB of values): up to six tiles
-//    are in flight per CU while two are in use; one barrier per tile, explicit vmcnt
-//    waits. The query rows of a segment arrive the same way (through four of the stages)
-//    so that the first tile's wait does not also wait for the rest of the prologue.
+//    into a ring of 8 stages of 16 KB (8 KB of keys + 8 KB of values): six tiles are in
+//    flight per CU while two are in use; explicit vmcnt waits and one barrier per tile.
+//    The query rows of a segment arrive the same way (through four of the stages).
 //    Each 256-byte LDS row holds its 16-byte chunks permuted by slot = chunk ^ f(row),
 //    f(row) = 4*(row%4) + (row/4)%4 (the permutation is applied on the global side of
 //    the copy). The K operand reads (ds_read_b128) serve 16 lanes = 16 consecutive rows
@@ -35,16 +33,18 @@
 //    conflict counter); per-lane read offsets are precomputed.
 //  * The score accumulator layout of the first MFMA is consumed directly as the P operand
 //    of the second (no shuffles): the V^T operand is read in the matching key order.
-//  * Software pipeline, one wave per SIMD: while the matrix core runs the QK products of
-//    tile t+1, the same wave's VALU computes the softmax of tile t (exp2, row sums, bf16
-//    packing); the PV products of tile t then overlap the row maxima of tile t+1. The
-//    loop is unrolled by two so that the score registers of consecutive tiles alternate
-//    without copies.
+//  * Two wave groups in antiphase ("ping-pong"): per tile a wave runs a matrix phase (QK
+//    products of tile j, PV products of tile j-1) and a vector phase (max, exp2, row sums
+//    and bf16 packing of tile j). Waves 0-3 run matrix then vector, waves 4-7 vector then
+//    matrix, so each SIMD's two waves keep its matrix core and its VALU busy at the same
+//    time. With 32 rows per wave everything fits in 256 VGPRs (no accumulation registers,
+//    no moves between register files).
 //  * Online softmax in the log2 domain; row max reduced across the two lane halves with
 //    v_permlane32_swap; the running max is only moved (and O rescaled) when a tile's max
 //    exceeds it by more than 2^8, which leaves the result unchanged and skips most
 //    rescales. Only the unit's last tile carries the key mask (a wave-uniform branch).
 //    Keys past ctx_len + S read the block's last row (finite data) and are masked to -inf.
+//    Row sums are taken over the bf16-rounded weights that the PV products use.
 //  * The epilogue stages each wave's O tile through LDS and writes whole 256-byte rows.
 //  * Built with IEEE mode off (no NaN reaches this kernel: padding is never read and the
 //    masked scores are -inf), so the row max is a plain v_max3 chain without the NaN
@@ -58,7 +58,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -68,24 +67,26 @@ constexpr int D = kAttnMfmaD;                 // 128
 constexpr int ROWB = D * 2;                   // 256-byte LDS rows
 constexpr int TB = KT * ROWB;                 // 8 KB per tensor tile
 constexpr int STAGEB = 2 * TB;                // K tile then V tile
-constexpr int NW = kAttnWaves;                // 4 waves
-constexpr int NTHR = NW * 64;                 // 256 threads
-constexpr int RPW = kAttnRowsPerWave;         // 64 query rows per wave
-constexpr int NB = RPW / 32;                  // 2 MFMA column blocks per wave
+constexpr int NW = kAttnWaves;                // 8 waves
+constexpr int NTHR = NW * 64;                 // 512 threads
+constexpr int RPW = kAttnRowsPerWave;         // 32 query rows per wave
 constexpr int RWG = kAttnRowsPerWg;           // 256 query rows per workgroup
-constexpr int DMA_PER_TENSOR = TB / 1024 / NW;  // 2 one-KB copies per wave per tensor
+constexpr int DMA_PER_TENSOR = TB / 1024 / NW;  // one 1-KB copy per wave per tensor
 constexpr int DMA_PER_TILE = 2 * DMA_PER_TENSOR;
-constexpr int DMA_Q = RPW * ROWB / 1024;      // 16 one-KB copies for a wave's query rows
+constexpr int DMA_Q = RPW * ROWB / 1024;      // 8 one-KB copies for a wave's query rows
 constexpr int NSTAGE = 8;                     // LDS ring
 constexpr int NPRO = 4;                       // tiles issued before the query rows are read
+constexpr int NAHEAD = 6;                     // tiles issued ahead of the one in the QK phase
 constexpr int OROWB = ROWB + 16;              // padded row of the epilogue staging
+constexpr int NDS = D / 16;                   // K operands per tile (d-steps)
+constexpr int NVO = 2 * (D / 32);             // V^T operands per tile, index i = ks * 4 + db
 constexpr float kLazy = 8.0f;                 // log2 headroom before the running max moves
 
 static_assert(NSTAGE * STAGEB >= (kMaxB + 1) * 4, "tile plan must fit in the ring");
-static_assert(NB == 2, "two column blocks per wave");
-static_assert(RPW * ROWB == STAGEB, "a wave's query rows fill one stage");
-static_assert(NPRO + NW == NSTAGE, "query rows use the stages after the prologue tiles");
+static_assert(RPW == 32 && DMA_PER_TENSOR == 1, "one MFMA column block and one copy per wave");
+static_assert(NW * RPW * ROWB == (NSTAGE - NPRO) * STAGEB, "query rows fill the stages after the prologue tiles");
 static_assert(NW * RPW * OROWB <= NSTAGE * STAGEB, "epilogue staging fits in the ring");
+static_assert(NAHEAD + 2 == NSTAGE, "two stages in use, the rest in flight");
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
@@ -154,8 +155,8 @@ __device__ void build_plan(int* P, int* wsum, const int32_t* ctx_len, int B, int
   __syncthreads();
 }
 
-// Source rows of one unit for the tile copies. This lane copies, for i = 0..1, the 16-byte
-// chunk c_i of tile row 8*wave + 4*i + lane/16 (c_i = (lane%16) ^ f(row)).
+// Source rows of one unit for the tile copies. This lane copies the 16-byte chunk
+// c = (lane%16) ^ f(row) of tile row 4*wave + lane/16 of each tensor.
 struct TileSrc {
   const char* kc;   // k_ctx row 0 of this unit (bytes; row stride rs)
   const char* vc;
@@ -163,8 +164,8 @@ struct TileSrc {
   const char* vb;
   size_t rs;        // Hkv * D * 2 bytes
   int nctx, S;
-  int coff[DMA_PER_TENSOR];  // c_i * 16
-  uint32_t voff[DMA_PER_TENSOR];  // (tile row of copy i of this lane) * rs + c_i * 16
+  int coff;         // c * 16
+  uint32_t voff;    // (tile row of this lane) * rs + c * 16
 };
 
 // One 16-byte-per-lane global -> LDS copy (global_load_lds_dwordx4): lane i's 16 bytes land
@@ -195,35 +196,25 @@ __device__ __forceinline__ uint32_t lds_addr(const char* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
 }
 
-// Issue the DMA copies of tile t into stage st: key j < ctx_len reads context row j, else
-// block row j - ctx_len; keys past ctx_len + S read the last block row (finite data whose
-// scores are masked). One wave-uniform LDS destination per copy (1 KB = 4 rows).
+// Issue this wave's copies of tile t into stage st: key j < ctx_len reads context row j,
+// else block row j - ctx_len; keys past ctx_len + S read the last block row (finite data
+// whose scores are masked). One wave-uniform LDS destination per copy (1 KB = 4 rows).
 __device__ __forceinline__ void issue_tile(const TileSrc& s, int t, char* st) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint32_t lds = lds_addr(st + 4 * w * ROWB);
   if ((t + 1) * KT <= __builtin_amdgcn_readfirstlane(s.nctx)) {
     // every key in the context: scalar bases, fixed lane offsets
     const size_t toff = (size_t)t * KT * s.rs;
-#pragma unroll
-    for (int i = 0; i < DMA_PER_TENSOR; ++i) {
-      const uint32_t lds = lds_addr(st + ((KT / NW) * w + 4 * i) * ROWB);
-      dma16s(s.kc + toff, s.voff[i], lds);
-      dma16s(s.vc + toff, s.voff[i], lds + TB);
-    }
+    dma16s(s.kc + toff, s.voff, lds);
+    dma16s(s.vc + toff, s.voff, lds + TB);
     return;
   }
-#pragma unroll
-  for (int i = 0; i < DMA_PER_TENSOR; ++i) {
-    const int row = (KT / NW) * w + 4 * i;
-    const int key = t * KT + row + (lane >> 4);
-    const bool in_ctx = key < s.nctx;
-    const int idx = in_ctx ? key : min(key - s.nctx, s.S - 1);
-    const size_t off = (size_t)idx * s.rs + s.coff[i];
-    const char* kp = (in_ctx ? s.kc : s.kb) + off;
-    const char* vp = (in_ctx ? s.vc : s.vb) + off;
-    const uint32_t lds = lds_addr(st + row * ROWB);
-    dma16(kp, lds);
-    dma16(vp, lds + TB);
-  }
+  const int key = t * KT + 4 * w + (lane >> 4);
+  const bool in_ctx = key < s.nctx;
+  const int idx = in_ctx ? key : min(key - s.nctx, s.S - 1);
+  const size_t off = (size_t)idx * s.rs + s.coff;
+  dma16((in_ctx ? s.kc : s.kb) + off, lds);
+  dma16((in_ctx ? s.vc : s.vb) + off, lds + TB);
 }
 
 // wait until at most n vector-memory operations of this wave are outstanding (n <= 63)
@@ -233,8 +224,8 @@ __device__ __forceinline__ void issue_tile(const TileSrc& s, int t, char* st) {
 
 __device__ __forceinline__ void wait_tiles_after(int n_after) {
   // n_after: tiles whose copies were issued after the one to be consumed (0..6)
-  if (n_after == 5) {  // the steady state of the tile loop
-    TT_WAIT_VM(5 * DMA_PER_TILE);
+  if (n_after == NAHEAD - 1) {  // the steady state of the tile loop
+    TT_WAIT_VM((NAHEAD - 1) * DMA_PER_TILE);
     return;
   }
   switch (n_after) {
@@ -257,239 +248,88 @@ __device__ __forceinline__ bf16x8 ld_v(const char* lo_p, const char* hi_p) {
   return __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
 }
 
-struct WaveState {
-  f32x16 oacc[D / 32][NB];
-  float m_run[NB], l_run[NB];
-};
-
 struct LaneOffsets {
-  int k[D / 16];          // K operand, d-step ds: row lr, chunk (2 ds + lh) ^ f(lr)
+  int k[NDS];             // K operand, d-step ds: row lr, chunk (2 ds + lh) ^ f(lr)
   int v[D / 32][2];       // V^T operand, head-dim block db, row half (+0 / +8)
 };
 
-constexpr int NDS = D / 16;       // K operands per tile (d-steps)
-constexpr int NVO = 2 * (D / 32);  // V^T operands per tile, index i = ks * 4 + db
+// Per-wave accumulation state of one segment.
+struct WaveState {
+  f32x16 oacc[D / 32];    // O^T, one 32x32 block per head-dim block
+  f32x16 s;               // scores S^T of the tile between its matrix and vector phases
+  bf16x8 pb[2];           // P of the tile between its vector phase and the next matrix phase
+  float m_run, l_run;
+};
 
-// K operands of one 32-key tile (one ds_read_b128 per d-step)
-__device__ __forceinline__ void load_k(const char* st, const LaneOffsets& lo, bf16x8 (&ka)[NDS]) {
+// LDS operand reads for a matrix phase: K operands of a tile (ds_read_b128 each) and the
+// V^T operands of a tile (two ds_read_b64_tr_b16 each).
+__device__ __forceinline__ void load_k_ops(const char* st, const LaneOffsets& lo, bf16x8 (&ka)[NDS]) {
 #pragma unroll
   for (int ds = 0; ds < NDS; ++ds) ka[ds] = ld_k(st + lo.k[ds]);
 }
 
-// V^T operands of one tile (two ds_read_b64_tr_b16 each)
-__device__ __forceinline__ void load_v(const char* st, const LaneOffsets& lo, bf16x8 (&va)[NVO]) {
+__device__ __forceinline__ void load_v_ops(const char* st, const LaneOffsets& lo, bf16x8 (&va)[NVO]) {
   const char* vt = st + TB;
 #pragma unroll
   for (int i = 0; i < NVO; ++i)
     va[i] = ld_v(vt + lo.v[i % 4][0] + (i / 4) * 16 * ROWB, vt + lo.v[i % 4][1] + (i / 4) * 16 * ROWB);
 }
 
-// S^T[key][query] = K Q^T of one 32-key tile for this wave's two column blocks; each K
-// operand feeds both.
-__device__ __forceinline__ void qk_mfma(const bf16x8 (&ka)[NDS], const bf16x8 (&qreg)[NB][D / 16],
-                                        f32x16 (&s)[NB]) {
-  const f32x16 zero = {};
+// Matrix phase: QK products of one tile (if do_qk) and PV products of the previous one
+// (if do_pv), from operands read during the preceding vector phase.
+__device__ __forceinline__ void matrix_phase(const bf16x8 (&ka)[NDS], const bf16x8 (&va)[NVO],
+                                             const bf16x8 (&qreg)[NDS], WaveState& w, bool do_qk,
+                                             bool do_pv) {
+  if (do_qk) {
+    const f32x16 zero = {};
 #pragma unroll
-  for (int ds = 0; ds < NDS; ++ds)
+    for (int ds = 0; ds < NDS; ++ds)
+      w.s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ds], qreg[ds], ds == 0 ? zero : w.s, 0, 0, 0);
+  }
+  if (do_pv) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-      s[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ds], qreg[nb][ds], ds == 0 ? zero : s[nb], 0, 0, 0);
-}
-
-__device__ __forceinline__ void qk_tile(const char* st, const LaneOffsets& lo,
-                                        const bf16x8 (&qreg)[NB][D / 16], f32x16 (&s)[NB]) {
-  bf16x8 ka[NDS];
-  load_k(st, lo, ka);
-  qk_mfma(ka, qreg, s);
-}
-
-// keys at or past nvalid get -inf (the unit's last tile only)
-__device__ __forceinline__ void mask_tile(f32x16 (&s)[NB], int key0, int nvalid, int lh) {
-  int lim = nvalid - key0 - 4 * lh;
-  asm volatile("" : "+v"(lim));  // keeps the compares inside the (rarely taken) branch
-#pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const int o = 8 * (k >> 2) + (k & 3);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-      if (o >= lim) s[nb][k] = -INFINITY;
+    for (int i = 0; i < NVO; ++i)
+      w.oacc[i % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], w.pb[i / 4], w.oacc[i % 4], 0, 0, 0);
   }
 }
 
-// row max of a tile in the log2 domain (scale_log2 > 0 commutes with max)
-__device__ __forceinline__ void tile_max(const f32x16 (&s)[NB], float scale_log2, float (&mx)[NB]) {
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    float m = s[nb][0];
-#pragma unroll
-    for (int k = 1; k < 16; ++k) m = __builtin_fmaxf(m, s[nb][k]);
-    mx[nb] = lane_pair_max(m) * scale_log2;
-  }
-}
-
-// move the running max (and rescale O and l) where a tile's max exceeds it by > 2^kLazy
-__device__ __forceinline__ void rescale(WaveState& w, const float (&mx)[NB]) {
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    if (__any(mx[nb] > w.m_run[nb] + kLazy)) {
-      const float mn = fmaxf(w.m_run[nb], mx[nb]);
-      const float alpha = __builtin_amdgcn_exp2f(w.m_run[nb] - mn);
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        // O lives in accumulation registers; the hints keep the allocator from moving it
-        // (for this rare VALU update) into the registers the tile loop needs
-        asm volatile("" : "+a"(w.oacc[db][nb]));
-#pragma unroll
-        for (int k = 0; k < 16; ++k) w.oacc[db][nb][k] *= alpha;
-        asm volatile("" : "+a"(w.oacc[db][nb]));
-      }
-      w.l_run[nb] *= alpha;
-      w.m_run[nb] = mn;
-    }
-  }
-}
-
-// P = exp2(s * scale_log2 - m), packed as the B operand of the PV products (key-step
-// ks = k / 8 holds the values k % 8); row sums into l
-__device__ __forceinline__ void softmax_tile(const f32x16 (&s)[NB], WaveState& w, float scale_log2,
-                                             bf16x8 (&pb)[NB][2]) {
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
+// Vector phase of a tile: key mask (the unit's last tile only), row max, lazy rescale,
+// P = exp2(s * scale_log2 - m) packed as the PV B operand (key-step ks = k / 8 holds
+// the values k % 8), and the row sums of the bf16-rounded P.
+__device__ __forceinline__ void vector_phase(WaveState& w, float scale_log2, bool mask, int lim) {
+  if (mask) {  // keys at or past nvalid get -inf; lim is opaque so the compares stay here
+    asm volatile("" : "+v"(lim));
 #pragma unroll
     for (int k = 0; k < 16; ++k)
-      pb[nb][k >> 3][k & 7] = (__bf16)__builtin_amdgcn_exp2f(s[nb][k] * scale_log2 - w.m_run[nb]);
-    // row sums of the bf16-rounded P, i.e. of exactly the weights the PV products use,
-    // two values per dot instruction
-    float ps0 = 0.0f, ps1 = 0.0f;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const bf16x2* pp = reinterpret_cast<const bf16x2*>(&pb[nb][ks]);
-      ps0 = __builtin_amdgcn_fdot2_f32_bf16(pp[0], ones, ps0, false);
-      ps1 = __builtin_amdgcn_fdot2_f32_bf16(pp[1], ones, ps1, false);
-      ps0 = __builtin_amdgcn_fdot2_f32_bf16(pp[2], ones, ps0, false);
-      ps1 = __builtin_amdgcn_fdot2_f32_bf16(pp[3], ones, ps1, false);
-    }
-    w.l_run[nb] += ps0 + ps1;
+      if (8 * (k >> 2) + (k & 3) >= lim) w.s[k] = -INFINITY;
   }
-}
-
-// O^T[d][query] += V^T P^T; each V operand feeds both column blocks
-__device__ __forceinline__ void pv_mfma(const bf16x8 (&va)[NVO], const bf16x8 (&pb)[NB][2], WaveState& w) {
+  float m = w.s[0];
 #pragma unroll
-  for (int i = 0; i < NVO; ++i)
+  for (int k = 1; k < 16; ++k) m = __builtin_fmaxf(m, w.s[k]);
+  const float mx = lane_pair_max(m) * scale_log2;  // scale_log2 > 0 commutes with max
+  if (__any(mx > w.m_run + kLazy)) {
+    const float mn = fmaxf(w.m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(w.m_run - mn);
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-      w.oacc[i % 4][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], pb[nb][i / 4], w.oacc[i % 4][nb], 0, 0, 0);
-}
-
-// Per-segment loop state.
-struct Seg {
-  TileSrc src;
-  LaneOffsets lo;
-  float scale_log2;
-  int ta, te, nt, nvalid, lh;
-};
-
-__device__ __forceinline__ char* stage_of(const Seg& g, int t) {
-  return g_ring + ((t - g.ta) & (NSTAGE - 1)) * STAGEB;
-}
-
-// One pipeline step: softmax and PV of tile t (scores in s, row max in mx); with NEXT also
-// the QK products of tile t+1 into sn and its row max into mx. The segment's last step
-// (NEXT false) applies the key mask when its tile is the unit's last one, and takes that
-// tile's max again; the other steps are one branch-free block after the rescale check, in
-// which the scheduler interleaves the two tiles' work.
-template <bool NEXT>
-__device__ __forceinline__ void step(const Seg& g, const bf16x8 (&qreg)[NB][D / 16], WaveState& ws,
-                                     f32x16 (&s)[NB], f32x16 (&sn)[NB], float (&mx)[NB], int t) {
-  if (NEXT) {
-    // tile t+1 complete for every wave; tiles issued after it: up to t+6
-    wait_tiles_after(__builtin_amdgcn_readfirstlane(min(5, g.te - 2 - t)));
-    __syncthreads();
-  } else if (__builtin_amdgcn_readfirstlane(t) == g.nt - 1) {
-    mask_tile(s, t * KT, g.nvalid, g.lh);
-    tile_max(s, g.scale_log2, mx);
-  }
-  rescale(ws, mx);
-
-  // The step body is written in issue order; sched_barrier keeps the compiler's
-  // scheduler from regrouping it. Each QK product of tile t+1 is followed by one piece of
-  // the softmax of tile t and by LDS operand reads spread over the phase: the K operands
-  // three d-steps ahead of their products, the V operands of tile t one per product (all
-  // in registers by the PV phase). Reads spread this way keep the LDS queue short: a
-  // wave stalled on a full LDS command queue cannot issue the arithmetic behind it.
-  const char* kst = stage_of(g, t + 1);
-  const char* vst = stage_of(g, t) + TB;
-  bf16x8 ka[NDS], va[NVO];
-  constexpr int KAHEAD = 3;
-  if (NEXT) {
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int ds = 0; ds < KAHEAD; ++ds) ka[ds] = ld_k(kst + g.lo.k[ds]);
+      for (int k = 0; k < 16; ++k) w.oacc[db][k] *= alpha;
+    w.l_run *= alpha;
+    w.m_run = mn;
   }
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  bf16x8 pb[NB][2];
-  float psum[NB][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
-  const f32x16 zero = {};
-  auto piece = [&](int i) {  // scores 2*(i%8), 2*(i%8)+1 of column block i/8
-    const int nb = i >> 3, k = 2 * (i & 7);
-    const float p0 = __builtin_amdgcn_exp2f(s[nb][k] * g.scale_log2 - ws.m_run[nb]);
-    const float p1 = __builtin_amdgcn_exp2f(s[nb][k + 1] * g.scale_log2 - ws.m_run[nb]);
+  float ps0 = 0.0f, ps1 = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 16; k += 2) {
     bf16x2 pp;
-    pp[0] = (__bf16)p0;
-    pp[1] = (__bf16)p1;
-    pb[nb][k >> 3][k & 7] = pp[0];
-    pb[nb][k >> 3][(k & 7) + 1] = pp[1];
-    psum[nb][i & 1] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, psum[nb][i & 1], false);
-  };
-  constexpr int NPC = 16, LEAD = 2;
-#pragma unroll
-  for (int i = 0; i < LEAD; ++i) piece(i);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int i = 0; i < NDS * NB; ++i) {
-    if (NEXT) {
-      const int ds = i >> 1, nb = i & 1;
-      sn[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ds], qreg[nb][ds], ds == 0 ? zero : sn[nb], 0, 0, 0);
-      if (nb == 1 && ds + KAHEAD < NDS) ka[ds + KAHEAD] = ld_k(kst + g.lo.k[ds + KAHEAD]);
-    }
-    if (i + LEAD < NPC) piece(i + LEAD);
-    if (i < NVO) va[i] = ld_v(vst + g.lo.v[i % 4][0] + (i / 4) * 16 * ROWB, vst + g.lo.v[i % 4][1] + (i / 4) * 16 * ROWB);
-    __builtin_amdgcn_sched_barrier(0);
+    pp[0] = (__bf16)__builtin_amdgcn_exp2f(w.s[k] * scale_log2 - w.m_run);
+    pp[1] = (__bf16)__builtin_amdgcn_exp2f(w.s[k + 1] * scale_log2 - w.m_run);
+    w.pb[k >> 3][k & 7] = pp[0];
+    w.pb[k >> 3][(k & 7) + 1] = pp[1];
+    if (k & 2) ps1 = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ps1, false);
+    else ps0 = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ps0, false);
   }
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) ws.l_run[nb] += psum[nb][0] + psum[nb][1];
-
-  // PV products of tile t. The scores of tile t+1 move to VGPRs in quarters (once, for
-  // its max and the next step's softmax) and are reduced to row maxima in between, late
-  // enough that its QK products have completed: column block 0 after PV product 4,
-  // column block 1 after product 9.
-  float mpart[NB];
-#pragma unroll
-  for (int j = 0; j < NVO * NB; ++j) {
-    const int i = j >> 1, nb = j & 1;
-    ws.oacc[i % 4][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], pb[nb][i / 4], ws.oacc[i % 4][nb], 0, 0, 0);
-    if (NEXT) {
-#pragma unroll
-      for (int cb = 0; cb < NB; ++cb) {
-        const int q = j - (4 + 5 * cb);  // quarter of column block cb handled after product j
-        if (q >= 0 && q < 4) {
-          f32x4 v = {sn[cb][4 * q], sn[cb][4 * q + 1], sn[cb][4 * q + 2], sn[cb][4 * q + 3]};
-          asm volatile("" : "+v"(v));
-#pragma unroll
-          for (int k = 0; k < 4; ++k) sn[cb][4 * q + k] = v[k];
-          const float m4 = __builtin_fmaxf(__builtin_fmaxf(v[0], v[1]), __builtin_fmaxf(v[2], v[3]));
-          mpart[cb] = q == 0 ? m4 : __builtin_fmaxf(mpart[cb], m4);
-        }
-        if (q == 4) mx[cb] = lane_pair_max(mpart[cb]) * g.scale_log2;
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  // the copies of tile t+7 (its stage held tile t-1, which every wave finished before
-  // this step's barrier); issued after the products so that a stalled issue of the
-  // copies delays no arithmetic of this step
-  if (NEXT && t + NSTAGE - 1 < g.te) issue_tile(g.src, t + NSTAGE - 1, stage_of(g, t + NSTAGE - 1));
+  w.l_run += ps0 + ps1;
 }
 
 // Partial slot of one (cluster, segment, query slice): O/l as bf16 [RWG][D], then m, l fp32.
@@ -508,7 +348,9 @@ __device__ __forceinline__ size_t qrow_bytes(const AttnArgs& a, int b, int g, in
 __global__ __launch_bounds__(NTHR, 1) void attn_mfma_kernel(AttnArgs a) {
   __shared__ int wsum[NW];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;  // 0: matrix phase first, 1: vector phase first
   const int lr = lane & 31, lh = lane >> 5;
   const int id = blockIdx.x;
   const int xcd = id & 7, kk = id >> 3;
@@ -541,13 +383,11 @@ __global__ __launch_bounds__(NTHR, 1) void attn_mfma_kernel(AttnArgs a) {
   char* Ob = static_cast<char*>(a.o);
   const int G = a.G, S = a.S, rows_unit = G * S;
 
-  Seg sg;
-  sg.scale_log2 = a.scale_log2;
-  sg.lh = lh;
+  LaneOffsets lo;
   {
     const int fk = swz(lr);
 #pragma unroll
-    for (int ds = 0; ds < D / 16; ++ds) sg.lo.k[ds] = lr * ROWB + (((2 * ds + lh) ^ fk) << 4);
+    for (int ds = 0; ds < NDS; ++ds) lo.k[ds] = lr * ROWB + (((2 * ds + lh) ^ fk) << 4);
     const int j = lane & 15, grp2 = (lane >> 4) & 1;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -556,16 +396,19 @@ __global__ __launch_bounds__(NTHR, 1) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
         const int c = 4 * db + 2 * grp2 + ((j & 3) >> 1);
-        sg.lo.v[db][h] = row * ROWB + ((c ^ fv) << 4) + (j & 1) * 8;
+        lo.v[db][h] = row * ROWB + ((c ^ fv) << 4) + (j & 1) * 8;
       }
     }
   }
-#pragma unroll
-  for (int i = 0; i < DMA_PER_TENSOR; ++i) {
-    const int row = (KT / NW) * wave + 4 * i + (lane >> 4);
-    sg.src.coff[i] = ((lane & 15) ^ swz(row & 15)) << 4;
-    sg.src.voff[i] = (uint32_t)(row * a.Hkv * D * 2 + sg.src.coff[i]);
+  TileSrc src;
+  {
+    const int row = 4 * wave + (lane >> 4);
+    src.coff = ((lane & 15) ^ swz(row & 15)) << 4;
+    src.voff = (uint32_t)(row * a.Hkv * D * 2 + src.coff);
+    src.rs = (size_t)a.Hkv * D * 2;
+    src.S = S;
   }
+  const float scale_log2 = a.scale_log2;
 
   int t = t0;
   bool first_seg = true;
@@ -587,123 +430,109 @@ __global__ __launch_bounds__(NTHR, 1) void attn_mfma_kernel(AttnArgs a) {
     first_seg = false;
     t = ustart + te;
     const int n = te - ta;  // tiles in this segment (>= 1)
+    const int nvalid = nctx + S;
     // an opaque copy of the lane id: the per-lane addresses of the prologue and epilogue
     // are then computed here rather than hoisted out of the segment loop and kept live
     // (in registers the tile loop needs) across it
     int ln = lane;
     asm volatile("" : "+v"(ln));
 
-    sg.ta = ta;
-    sg.te = te;
-    sg.nt = nt;
-    sg.nvalid = nctx + S;
-    {
-      const size_t rsb = (size_t)a.Hkv * D * 2;
-      sg.src.rs = rsb;
-      sg.src.kc = static_cast<const char*>(a.k_ctx) + ((size_t)bcur * a.Lmax * a.Hkv + g) * D * 2;
-      sg.src.vc = static_cast<const char*>(a.v_ctx) + ((size_t)bcur * a.Lmax * a.Hkv + g) * D * 2;
-      sg.src.kb = static_cast<const char*>(a.k_blk) + ((size_t)bcur * S * a.Hkv + g) * D * 2;
-      sg.src.vb = static_cast<const char*>(a.v_blk) + ((size_t)bcur * S * a.Hkv + g) * D * 2;
-      sg.src.nctx = nctx;
-      sg.src.S = S;
-    }
+    src.kc = static_cast<const char*>(a.k_ctx) + ((size_t)bcur * a.Lmax * a.Hkv + g) * D * 2;
+    src.vc = static_cast<const char*>(a.v_ctx) + ((size_t)bcur * a.Lmax * a.Hkv + g) * D * 2;
+    src.kb = static_cast<const char*>(a.k_blk) + ((size_t)bcur * S * a.Hkv + g) * D * 2;
+    src.vb = static_cast<const char*>(a.v_blk) + ((size_t)bcur * S * a.Hkv + g) * D * 2;
+    src.nctx = nctx;
+    auto stage = [&](int k) { return g_ring + (k & (NSTAGE - 1)) * STAGEB; };  // local tile k
 
-    // ---- prologue. Query rows of this wave -> stage NPRO + wave (row j of the wave at LDS
-    // row j, chunks permuted like the key tiles); row r of the unit is (head-in-group r / S,
-    // position r % S); rows past the unit read its row 0 (results discarded).
+    // ---- prologue. Query rows of this wave -> its 8 KB behind the first NPRO stages (row
+    // j of the wave at LDS row j, chunks permuted like the key tiles); row r of the unit is
+    // (head-in-group r / S, position r % S); rows past the unit read its row 0 (results
+    // discarded).
     const int row0 = qs * RWG + wave * RPW;  // this wave's first unit row
-    {
-      char* qst = g_ring + (NPRO + wave) * STAGEB;
+    char* qst = g_ring + NPRO * STAGEB + wave * RPW * ROWB;
 #pragma unroll
-      for (int i = 0; i < DMA_Q; ++i) {
-        const int j = 4 * i + (ln >> 4);
-        const int r = row0 + j;
-        const int c = (ln & 15) ^ swz(j & 15);
-        dma16(Qb + qrow_bytes(a, bcur, g, r < rows_unit ? r : 0) + (c << 4), lds_addr(qst + 4 * i * ROWB));
-      }
+    for (int i = 0; i < DMA_Q; ++i) {
+      const int j = 4 * i + (ln >> 4);
+      const int r = row0 + j;
+      const int c = (ln & 15) ^ swz(j & 15);
+      dma16(Qb + qrow_bytes(a, bcur, g, r < rows_unit ? r : 0) + (c << 4), lds_addr(qst + 4 * i * ROWB));
     }
     const int npro = min(n, NPRO);
-    for (int k = 0; k < npro; ++k) issue_tile(sg.src, ta + k, stage_of(sg, ta + k));
+    for (int k = 0; k < npro; ++k) issue_tile(src, ta + k, stage(k));
     switch (npro) {  // this wave's query rows have landed
       case 1: TT_WAIT_VM(1 * DMA_PER_TILE); break;
       case 2: TT_WAIT_VM(2 * DMA_PER_TILE); break;
       case 3: TT_WAIT_VM(3 * DMA_PER_TILE); break;
       default: TT_WAIT_VM(4 * DMA_PER_TILE); break;
     }
-    bf16x8 qreg[NB][D / 16];
-    {
-      const char* qst = g_ring + (NPRO + wave) * STAGEB;
+    bf16x8 qreg[NDS];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int ds = 0; ds < D / 16; ++ds) {
-          qreg[nb][ds] = ld_k(qst + nb * 32 * ROWB + sg.lo.k[ds]);
-          // the query operands stay in accumulation registers (MFMA sources may be read
-          // from there), leaving the VGPRs to the softmax
-          asm volatile("" : "+a"(qreg[nb][ds]));
-        }
-    }
+    for (int ds = 0; ds < NDS; ++ds) qreg[ds] = ld_k(qst + lo.k[ds]);
     TT_WAIT_LGKM0();
     __syncthreads();  // every wave has its query rows: their stages take tiles now
-    for (int k = NPRO; k < min(n, NSTAGE - 1); ++k) issue_tile(sg.src, ta + k, stage_of(sg, ta + k));
-    wait_tiles_after(__builtin_amdgcn_readfirstlane(min(n, NSTAGE - 1) - 1));  // tile ta
+    for (int k = NPRO; k < min(n, NAHEAD); ++k) issue_tile(src, ta + k, stage(k));
+    wait_tiles_after(__builtin_amdgcn_readfirstlane(min(n, NAHEAD) - 1));  // local tile 0
     __syncthreads();
 
     WaveState ws;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int k = 0; k < 16; ++k) ws.oacc[db][nb][k] = 0.0f;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      ws.m_run[nb] = -INFINITY;
-      ws.l_run[nb] = 0.0f;
-    }
+      for (int k = 0; k < 16; ++k) ws.oacc[db][k] = 0.0f;
+    ws.m_run = -INFINITY;
+    ws.l_run = 0.0f;
 
-    f32x16 sA[NB], sB[NB];
-    float mx[NB];
-    qk_tile(stage_of(sg, ta), sg.lo, qreg, sA);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+v"(sA[nb]));
-    tile_max(sA, sg.scale_log2, mx);
-
-    // ---- pipelined loop, unrolled by two (scores alternate between sA and sB)
-    int tt = ta;
-    for (; tt + 2 < te; tt += 2) {
-      step<true>(sg, qreg, ws, sA, sB, mx, tt);
-      step<true>(sg, qreg, ws, sB, sA, mx, tt + 1);
+    // ---- tile loop, one code path for both wave groups. Iteration j: matrix phase (QK
+    // products of tile j, PV products of tile j-1), barrier, vector phase (tile j; it
+    // first issues the LDS reads of the next matrix phase: K of tile j+1, V of tile j, so
+    // their latency passes behind its arithmetic), barrier. Group 1 passes one extra
+    // barrier first, so it runs each phase while group 0 runs the other one (the barriers
+    // pair group 0's k-th with group 1's (k-1)-th; each SIMD holds one wave of each group).
+    // Tile j+1 is published by the barrier that starts group 0's vector phase j: before it
+    // each wave waits for its own copies of that tile (group 0 after matrix phase j, group
+    // 1 after vector phase j-1). A wave issues its copies of tile j+6 at the start of its
+    // matrix phase j, into the stage of tile j-2, whose last reads (vector phase j-2) both
+    // groups finished two barriers earlier.
+    bf16x8 ka[NDS], va[NVO];
+    load_k_ops(stage(0), lo, ka);
+    if (grp == 1) {
+      if (1 < n) wait_tiles_after(__builtin_amdgcn_readfirstlane(min(NAHEAD - 2, n - 2)));
+      __syncthreads();
     }
-    if (tt + 1 < te) {
-      step<true>(sg, qreg, ws, sA, sB, mx, tt);
-      step<false>(sg, qreg, ws, sB, sA, mx, tt + 1);
-    } else {
-      step<false>(sg, qreg, ws, sA, sB, mx, tt);
+    for (int j = 0; j <= n; ++j) {
+      if (j + NAHEAD < n) issue_tile(src, ta + j + NAHEAD, stage(j + NAHEAD));
+      matrix_phase(ka, va, qreg, ws, j < n, j >= 1);
+      if (grp == 0 && j + 1 < n) wait_tiles_after(__builtin_amdgcn_readfirstlane(min(NAHEAD - 1, n - 2 - j)));
+      __syncthreads();
+      if (j + 1 < n) load_k_ops(stage(j + 1), lo, ka);
+      if (j < n) load_v_ops(stage(j), lo, va);
+      __builtin_amdgcn_sched_barrier(0);
+      if (j < n) vector_phase(ws, scale_log2, ta + j == nt - 1, nvalid - (ta + j) * KT - 4 * lh);
+      if (grp == 1 && j + 2 < n) wait_tiles_after(__builtin_amdgcn_readfirstlane(min(NAHEAD - 2, n - 3 - j)));
+      __syncthreads();
     }
-    __syncthreads();  // every wave is done with the stages
+    if (grp == 0) __syncthreads();
 
     // ---- epilogue: O / l as bf16 through this wave's LDS staging rows, then whole rows
     // to the output, or to a partial slot with m and l
     char* ost = g_ring + wave * RPW * OROWB;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const float lt = lane_pair_sum(ws.l_run[nb]);
+    {
+      const float lt = lane_pair_sum(ws.l_run);
       const float inv = 1.0f / lt;
-      char* orow = ost + (nb * 32 + (ln & 31)) * OROWB;
+      char* orow = ost + (ln & 31) * OROWB;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           bf16x4 v;
 #pragma unroll
-          for (int k = 0; k < 4; ++k) v[k] = (__bf16)(ws.oacc[db][nb][q4 * 4 + k] * inv);
+          for (int k = 0; k < 4; ++k) v[k] = (__bf16)(ws.oacc[db][q4 * 4 + k] * inv);
           *reinterpret_cast<u32x2*>(orow + (db * 32 + 8 * q4 + 4 * (ln >> 5)) * 2) = __builtin_bit_cast(u32x2, v);
         }
       if (!whole && ln < 32) {
         float* ml = reinterpret_cast<float*>(part_slot(a, cluster, slot, qs) + (size_t)RWG * D * 2);
-        const int rw = wave * RPW + nb * 32 + ln;
-        ml[rw] = ws.m_run[nb];
+        const int rw = wave * RPW + ln;
+        ml[rw] = ws.m_run;
         ml[RWG + rw] = lt;
       }
     }

@@ -15,8 +15,8 @@ namespace tt {
 // ---------------------------------------------------------------------------------------
 
 constexpr int kAttnKeysPerTile = 32;   // keys staged in LDS per pipeline step
-constexpr int kAttnWaves = 4;          // waves per workgroup of the MFMA kernel
-constexpr int kAttnRowsPerWave = 64;   // query rows (head-in-group x block position) per wave
+constexpr int kAttnWaves = 8;          // waves per workgroup of the MFMA kernel
+constexpr int kAttnRowsPerWave = 32;   // query rows (head-in-group x block position) per wave
 constexpr int kAttnRowsPerWg = kAttnWaves * kAttnRowsPerWave;
 constexpr int kAttnMfmaD = 128;        // head dim of the MFMA kernel
 constexpr int kMaxB = 8191;            // largest batch (the tile plan sits in LDS)
