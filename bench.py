@@ -42,6 +42,34 @@ def attn_flops(x) -> float:
     return float(4 * x.S * x.Hq * x.D * int(n.sum()))
 
 
+PROFILE_MD = os.path.join(ROOT, "profiles", "kernels_b32_s16_ctx8k_bf16.md")
+
+
+def attn_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("attn_mfma.hip", "tt_internal.h"):
+        with open(os.path.join(ROOT, "block_diffusion_lm_tt_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary (FETCH_SIZE and
+    WRITE_SIZE, each scaled by a plain copy's reading), or None when that summary was taken
+    on another version of the kernel source than the one built here."""
+    try:
+        text = open(PROFILE_MD).read()
+    except OSError:
+        return None
+    import re
+    m = re.search(r"attention source sha256\[:16\][^`]*`([0-9a-f]+)`", text)
+    t = re.search(kernel + r" traffic_bytes_per_launch: (\d+)", text)
+    if not m or not t or m.group(1) != attn_source_hash():
+        return None
+    return int(t.group(1))
+
+
 def cpu_baseline(w, budget_s: float) -> dict:
     """The fp64 oracle as it stands, on this host, on a bounded sample of the workload."""
     from oracle import ttref_block_denoise_attn, ttref_threads
@@ -82,9 +110,10 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "the hot path has no multi-GPU collective and this build does not run on more than one "
-              "GPU.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "the hot path has no collective; sequences and KV heads shard across GPUs with no "
+              "exchange, so a multi-GPU figure would be N independent copies of this one.",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -199,8 +228,8 @@ def main():
         "mfma_pct_bf16_peak": 100.0 * tflops / MFMA_BF16_PEAK_TFLOPS,
         "roofline": {"kernel": "attn_mfma_kernel", "bound": "hbm", "achieved": gbs_main,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs_main / HBM_PEAK_GBS,
-                     "traffic": None, "avg_us": t_main * 1e6,
-                     "algorithmic_bytes_per_launch": kv_bytes},
+                     "traffic": profiled_traffic("attn_mfma_kernel") if args.config == 3 else None,
+                     "avg_us": t_main * 1e6, "algorithmic_bytes_per_launch": kv_bytes},
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

@@ -44,7 +44,6 @@
 //    exceeds it by more than 2^8, which leaves the result unchanged and skips most
 //    rescales. Only the unit's last tile carries the key mask (a wave-uniform branch).
 //    Keys past ctx_len + S read the block's last row (finite data) and are masked to -inf.
-//    Row sums are taken over the bf16-rounded weights that the PV products use.
 //  * The epilogue stages each wave's O tile through LDS and writes whole 256-byte rows.
 //  * Built with IEEE mode off (no NaN reaches this kernel: padding is never read and the
 //    masked scores are -inf), so the row max is a plain v_max3 chain without the NaN
@@ -303,11 +302,15 @@ __device__ __forceinline__ void vector_phase(WaveState& w, float scale_log2, boo
     for (int k = 0; k < 16; ++k)
       if (8 * (k >> 2) + (k & 3) >= lim) w.s[k] = -INFINITY;
   }
+  // Each lane half holds 16 of the tile's 32 keys for its row. The half maxima decide
+  // whether the running max may stay (every half within 2^kLazy of it, so is the row);
+  // only when some lane's half exceeds it are the two halves combined (v_permlane32_swap,
+  // a slow instruction) and O, l rescaled, identically in both halves.
   float m = w.s[0];
 #pragma unroll
   for (int k = 1; k < 16; ++k) m = __builtin_fmaxf(m, w.s[k]);
-  const float mx = lane_pair_max(m) * scale_log2;  // scale_log2 > 0 commutes with max
-  if (__any(mx > w.m_run + kLazy)) {
+  if (__any(m * scale_log2 > w.m_run + kLazy)) {
+    const float mx = lane_pair_max(m) * scale_log2;  // scale_log2 > 0 commutes with max
     const float mn = fmaxf(w.m_run, mx);
     const float alpha = __builtin_amdgcn_exp2f(w.m_run - mn);
 #pragma unroll
@@ -317,17 +320,17 @@ __device__ __forceinline__ void vector_phase(WaveState& w, float scale_log2, boo
     w.l_run *= alpha;
     w.m_run = mn;
   }
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  // P in bf16 for the PV products; the row sum in fp32 from the unrounded values (plain
+  // adds: the dot instructions contend with the other wave's matrix products)
   float ps0 = 0.0f, ps1 = 0.0f;
 #pragma unroll
   for (int k = 0; k < 16; k += 2) {
-    bf16x2 pp;
-    pp[0] = (__bf16)__builtin_amdgcn_exp2f(w.s[k] * scale_log2 - w.m_run);
-    pp[1] = (__bf16)__builtin_amdgcn_exp2f(w.s[k + 1] * scale_log2 - w.m_run);
-    w.pb[k >> 3][k & 7] = pp[0];
-    w.pb[k >> 3][(k & 7) + 1] = pp[1];
-    if (k & 2) ps1 = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ps1, false);
-    else ps0 = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ps0, false);
+    const float p0 = __builtin_amdgcn_exp2f(w.s[k] * scale_log2 - w.m_run);
+    const float p1 = __builtin_amdgcn_exp2f(w.s[k + 1] * scale_log2 - w.m_run);
+    w.pb[k >> 3][k & 7] = (__bf16)p0;
+    w.pb[k >> 3][(k & 7) + 1] = (__bf16)p1;
+    ps0 += p0;
+    ps1 += p1;
   }
   w.l_run += ps0 + ps1;
 }
