@@ -95,6 +95,84 @@ def cpu_baseline(w, budget_s: float) -> dict:
                       f"{t_total:.1f} s, rate rescaled to the batch's mean context length"}
 
 
+def loop_bench(w, args, torch, tt, TZ, W):
+    """Block loop (the block-loop workload): per block, T denoising steps; each step runs
+    tt_block_denoise_attn on every layer (its own context KV, block Q/K/V drawn per
+    (step, layer)) and then tt_commit on that step's logits; the still-masked set shrinks
+    by the committed positions, and the last step commits whatever is left (the end of a
+    block). Reported per gamma: blocks/s = B / (time of the T steps) and the positions
+    committed at each step. Inputs are generated and copied to HBM before timing."""
+    dev = torch.device("cuda:0")
+    T, L = w.steps, w.layers
+    log(f"[loop] generating workload {w.cid}: {w.name}")
+    ctx = torch.from_numpy(w.ctx_lens()).to(dev)
+    kcs, vcs = [], []
+    for l in range(L):
+        x = w.attn(step=0, layer=l)
+        _, _, _, kc, vc, _ = TZ.attn_to_device(x, dev)
+        kcs.append(kc)
+        vcs.append(vc)
+        del x
+    qkv = [[tuple(TZ.to_torch(a, w.dtype, dev) for a in w.block_qkv(t, l)) for l in range(L)]
+           for t in range(T)]
+    logits = [TZ.commit_to_device(w.commit(step=t), dev)[0] for t in range(T)]
+    out = torch.empty_like(qkv[0][0][0])
+    dt = 1 if w.dtype == W.BF16 else 0
+    ws_a = torch.empty(max(1, tt.tt_block_denoise_attn_workspace(w.B, w.S, w.Hq, w.Hkv, w.D, w.Lmax, dt)),
+                       dtype=torch.uint8, device=dev)
+    ws_c = torch.empty(max(1, tt.tt_commit_workspace(w.B, w.S, w.V, dt)), dtype=torch.uint8, device=dev)
+    tok = torch.empty((w.B, w.S), dtype=torch.int32, device=dev)
+    com = torch.empty((w.B, w.S), dtype=torch.uint8, device=dev)
+    mask = torch.empty((w.B, w.S), dtype=torch.uint8, device=dev)
+    counts = torch.zeros((T,), dtype=torch.int64, device=dev)
+    ones = torch.ones((w.B, w.S), dtype=torch.uint8, device=dev)
+
+    def block(gamma: float):
+        mask.copy_(ones)
+        for t in range(T):
+            for l in range(L):
+                q, kb, vb = qkv[t][l]
+                tt.tt_block_denoise_attn(q, kb, vb, kcs[l], vcs[l], ctx, out=out, workspace=ws_a)
+            tt.tt_commit(logits[t], mask, gamma, token_id=tok, committed=com, workspace=ws_c,
+                         want_conf=False)
+            if t == T - 1:
+                com.copy_(mask)  # end of the block: every remaining masked position commits
+            counts[t] += com.sum()
+            mask.sub_(com)  # committed positions are masked ones: mask & ~committed
+
+    results = []
+    reps = max(1, args.steps // 10)
+    for gamma in (0.5, 0.8, 0.95):
+        for _ in range(max(1, args.warmup // 10)):
+            block(gamma)
+        torch.cuda.synchronize()
+        counts.zero_()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            block(gamma)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        per_step = (counts.double() / reps / w.B).tolist()
+        results.append({"gamma": gamma, "blocks_per_s": w.B / (ms * 1e-3), "ms_per_block": ms,
+                        "tokens_per_step_per_sequence": per_step,
+                        "threshold_commits_per_sequence": sum(per_step[:-1]),
+                        "end_of_block_commits_per_sequence": per_step[-1]})
+        log(f"[loop] gamma {gamma}: {ms:.3f} ms per block of {T} steps x {L} layers, "
+            f"{w.B / (ms * 1e-3):.1f} blocks/s, committed per step per sequence {per_step}")
+    attn_flop = 4.0 * w.S * w.Hq * w.D * float((w.ctx_lens().astype(np.int64) + w.S).sum()) * L * T
+    res = {"metric": "block-loop blocks/s and tokens committed per step", "unit": "blocks/s",
+           "value": results[1]["blocks_per_s"], "n_gpus": 1, "higher_is_better": True,
+           "dtype": "bf16", "data": "synthetic (seeded)",
+           "config": {"workload": w.name, "B": w.B, "S": w.S, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
+                      "ctx_len": int(w.ctx_lens()[0]), "layers": L, "steps": T, "V": w.V,
+                      "reps": reps},
+           "attn_mfma_TFLOPs_gamma_0.8": attn_flop / (results[1]["ms_per_block"] * 1e-3) / 1e12,
+           "sweep": results}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -129,9 +207,8 @@ def main():
     tt.lib()
     w = W.WORKLOADS[args.config]
     if w.layers != 1:
-        print("bench.py times a single-layer workload (1-4); the block loop is bench_loop.py",
-              file=sys.stderr)
-        sys.exit(2)
+        loop_bench(w, args, torch, tt, TZ, W)
+        return
 
     log(f"[bench] generating workload {w.cid}: {w.name}")
     x = w.attn()

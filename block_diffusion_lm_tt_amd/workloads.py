@@ -165,6 +165,16 @@ def make_attn(B: int, S: int, Hq: int, Hkv: int, D: int, ctx_lens: Sequence[int]
                       _encode(vb, dtype), kc_e, vc_e, ctx)
 
 
+def make_block_qkv(B: int, S: int, Hq: int, Hkv: int, D: int, dtype: str = BF16, seed: int = 0,
+                   step: int = 0, layer: int = 0):
+    """The block's (q, k_blk, v_blk) of one (step, layer): the same draws as ``make_attn``
+    (without hot keys), without drawing the context again."""
+    q = _normal(_rng(seed, _T_Q, step, layer), (B, S, Hq, D))
+    kb = _normal(_rng(seed, _T_KB, step, layer), (B, S, Hkv, D))
+    vb = _normal(_rng(seed, _T_VB, step, layer), (B, S, Hkv, D))
+    return _encode(q, dtype), _encode(kb, dtype), _encode(vb, dtype)
+
+
 def make_commit(B: int, S: int, V: int, dtype: str = BF16, sigma: float = 3.0, seed: int = 0,
                 step: int = 0, gamma: float = 0.8, mask: Optional[np.ndarray] = None,
                 peaks: Optional[dict] = None) -> CommitInputs:
@@ -248,6 +258,11 @@ class Workload:
         hot = {"frac": 0.01, "boost": 8.0, "bias_norm": 2.0} if self.cid == 4 else None
         return make_attn(nb, self.S, self.Hq, self.Hkv, self.D, ctx[:nb], Lmax=self.Lmax,
                          dtype=self.dtype, seed=self.seed, step=step, layer=layer, hot_keys=hot)
+
+    def block_qkv(self, step: int, layer: int):
+        """(q, k_blk, v_blk) of one denoising step and layer (block-loop workload)."""
+        return make_block_qkv(self.B, self.S, self.Hq, self.Hkv, self.D, self.dtype, self.seed, step,
+                              layer)
 
     def commit(self, step: int = 0, gamma: Optional[float] = None, B: Optional[int] = None,
                mask: Optional[np.ndarray] = None) -> CommitInputs:
