@@ -566,15 +566,22 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const int rows_unit = a.G * a.S;
   const int r = blockIdx.y * 16 + (threadIdx.x >> 4);
   const int d = (threadIdx.x & 15) * 8;
-  const int T = a.plan[a.B];
-  const int pb = a.plan[b];
-  const int nt = (a.plan[b + 1] - pb) / a.Hkv;
+  // the plan was written by the previous kernel: scalar loads, uniform arithmetic
+  const c_i32* plan = (c_i32*)(uintptr_t)a.plan;
+  const int T = plan[a.B];
+  const int pb = plan[b];
+  const int nt = (plan[b + 1] - pb) / a.Hkv;
   const int start = pb + g * nt, end = start + nt;
   // cluster c owns [c*T/NC, (c+1)*T/NC); the one holding tile x is ceil((x+1)*NC/T) - 1
   const int c_first = (int)((((long long)start + 1) * a.NC + T - 1) / T) - 1;
   const int c_last = (int)((((long long)end) * a.NC + T - 1) / T) - 1;
   if (c_first == c_last) return;  // one cluster saw the whole unit and wrote it already
   if (r >= rows_unit) return;
+  // the first piece is its cluster's second segment when that cluster's range starts
+  // before the unit; every later piece is its cluster's first segment. With T >= NC no
+  // cluster range is empty.
+  const int first_slot = (int)(((long long)c_first * T) / a.NC) < start ? 1 : 0;
+  const bool may_be_empty = T < a.NC;
   const int qsl = r / RWG, rw = r - qsl * RWG;
   float M = -INFINITY, L = 0.0f, o[8];
 #pragma unroll
@@ -585,14 +592,14 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 #pragma unroll
     for (int j = 0; j < PB; ++j) {
       const int c = c0 + j;
-      const int r0 = (int)(((long long)c * T) / a.NC);
-      const bool ok = c <= c_last && r0 != (int)(((long long)(c + 1) * T) / a.NC);  // non-empty
+      bool ok = c <= c_last;
+      if (may_be_empty && ok)
+        ok = ((long long)c * T) / a.NC != ((long long)(c + 1) * T) / a.NC;
       mv[j] = -INFINITY;
       lv[j] = 0.0f;
       ov[j] = u32x4{0, 0, 0, 0};
       if (ok) {
-        const int slot = (start <= r0) ? 0 : 1;
-        const char* base = part_slot(a, c, slot, qsl);
+        const char* base = part_slot(a, c, c == c_first ? first_slot : 0, qsl);
         const float* ml = reinterpret_cast<const float*>(base + (size_t)RWG * D * 2);
         mv[j] = ml[rw];
         lv[j] = ml[RWG + rw];
