@@ -83,13 +83,22 @@ constexpr float kLazy = 8.0f;                 // log2 headroom before the runnin
 
 static_assert(NSTAGE * STAGEB >= (kMaxB + 1) * 4, "tile plan must fit in the ring");
 static_assert(RPW == 32 && DMA_PER_TENSOR == 1, "one MFMA column block and one copy per wave");
-static_assert(NW * RPW * ROWB == (NSTAGE - NPRO) * STAGEB, "query rows fill the stages after the prologue tiles");
+static_assert(RPW * ROWB == TB && NW == 2 * (NSTAGE - NPRO), "query rows fill the stages after the prologue tiles");
 static_assert(NW * RPW * OROWB <= NSTAGE * STAGEB, "epilogue staging fits in the ring");
 static_assert(NAHEAD + 2 == NSTAGE, "two stages in use, the rest in flight");
+static_assert(NSTAGE * TB == 65536, "immediate LDS offsets cover one tensor's stages");
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-__shared__ __attribute__((aligned(1024))) char g_ring[NSTAGE * STAGEB];
+// The ring holds the K tiles of the 8 stages in its first 64 KB and the V tiles in the
+// next 64 KB, so that every LDS operand read of a stage is a fixed per-lane register plus
+// an immediate offset below 64 KB. It is the kernel's only LDS variable (at address 0);
+// its last 64 bytes are the plan's per-wave sums.
+constexpr int VOFF = NSTAGE * TB;
+__shared__ __attribute__((aligned(1024))) char g_ring[NSTAGE * STAGEB + 64];
+
+__device__ __forceinline__ char* kst(int s) { return g_ring + s * TB; }
+__device__ __forceinline__ char* vst(int s) { return g_ring + VOFF + s * TB; }
 
 __device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 
@@ -177,15 +186,19 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
                : "memory", "m0");
 }
 
-// The same copy from a wave-uniform base (scalar registers) plus a 32-bit per-lane offset.
-__device__ __forceinline__ void dma16s(const char* base, uint32_t voff, uint32_t lds) {
-  // the two halves through scalar registers; readfirstlane yields a signed int, so each
-  // half is taken as uint32_t before widening (a sign-extended low half would corrupt
-  // the high word)
-  const uint64_t v = (uint64_t)(uintptr_t)base;
+// A wave-uniform pointer moved to scalar registers: the two halves through readfirstlane,
+// which yields a signed int, so each half is taken as uint32_t before widening (a
+// sign-extended low half would corrupt the high word).
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
   const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
   const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  base = reinterpret_cast<const char*>((uintptr_t)((hi << 32) | lo));
+  return reinterpret_cast<const char*>((uintptr_t)((hi << 32) | lo));
+}
+
+// The same copy from a wave-uniform base (scalar registers) plus a 32-bit per-lane offset.
+__device__ __forceinline__ void dma16s(const char* base, uint32_t voff, uint32_t lds) {
+  base = uniform_ptr(base);
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:0" ::"v"(voff),
                "s"(base), "s"(lds)
                : "memory", "m0");
@@ -198,22 +211,30 @@ __device__ __forceinline__ uint32_t lds_addr(const char* p) {
 // Issue this wave's copies of tile t into stage st: key j < ctx_len reads context row j,
 // else block row j - ctx_len; keys past ctx_len + S read the last block row (finite data
 // whose scores are masked). One wave-uniform LDS destination per copy (1 KB = 4 rows).
-__device__ __forceinline__ void issue_tile(const TileSrc& s, int t, char* st) {
+__device__ __forceinline__ void issue_tile(const TileSrc& s, int t, int st) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const uint32_t lds = lds_addr(st + 4 * w * ROWB);
+  const uint32_t ldk = lds_addr(kst(st) + 4 * w * ROWB), ldv = ldk + VOFF;
   if ((t + 1) * KT <= __builtin_amdgcn_readfirstlane(s.nctx)) {
     // every key in the context: scalar bases, fixed lane offsets
     const size_t toff = (size_t)t * KT * s.rs;
-    dma16s(s.kc + toff, s.voff, lds);
-    dma16s(s.vc + toff, s.voff, lds + TB);
+    dma16s(s.kc + toff, s.voff, ldk);
+    dma16s(s.vc + toff, s.voff, ldv);
     return;
   }
   const int key = t * KT + 4 * w + (lane >> 4);
   const bool in_ctx = key < s.nctx;
   const int idx = in_ctx ? key : min(key - s.nctx, s.S - 1);
   const size_t off = (size_t)idx * s.rs + s.coff;
-  dma16((in_ctx ? s.kc : s.kb) + off, lds);
-  dma16((in_ctx ? s.vc : s.vb) + off, lds + TB);
+  dma16((in_ctx ? s.kc : s.kb) + off, ldk);
+  dma16((in_ctx ? s.vc : s.vb) + off, ldv);
+}
+
+// The steady-state copy: a scalar base (already wave-uniform, in scalar registers) plus
+// the lane offset.
+__device__ __forceinline__ void dma16u(const char* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:0" ::"v"(voff),
+               "s"(base), "s"(lds)
+               : "memory", "m0");
 }
 
 // wait until at most n vector-memory operations of this wave are outstanding (n <= 63)
@@ -249,7 +270,7 @@ __device__ __forceinline__ bf16x8 ld_v(const char* lo_p, const char* hi_p) {
 
 struct LaneOffsets {
   int k[NDS];             // K operand, d-step ds: row lr, chunk (2 ds + lh) ^ f(lr)
-  int v[D / 32][2];       // V^T operand, head-dim block db, row half (+0 / +8)
+  int v[D / 32][2];       // V^T operand, head-dim block db, row half (+0 / +8); + VOFF
 };
 
 // Per-wave accumulation state of one segment.
@@ -267,11 +288,11 @@ __device__ __forceinline__ void load_k_ops(const char* st, const LaneOffsets& lo
   for (int ds = 0; ds < NDS; ++ds) ka[ds] = ld_k(st + lo.k[ds]);
 }
 
+// (st: the stage's K tile; the V^T lane offsets include the distance to its V tile)
 __device__ __forceinline__ void load_v_ops(const char* st, const LaneOffsets& lo, bf16x8 (&va)[NVO]) {
-  const char* vt = st + TB;
 #pragma unroll
   for (int i = 0; i < NVO; ++i)
-    va[i] = ld_v(vt + lo.v[i % 4][0] + (i / 4) * 16 * ROWB, vt + lo.v[i % 4][1] + (i / 4) * 16 * ROWB);
+    va[i] = ld_v(st + lo.v[i % 4][0] + (i / 4) * 16 * ROWB, st + lo.v[i % 4][1] + (i / 4) * 16 * ROWB);
 }
 
 // Matrix phase: QK products of one tile (if do_qk) and PV products of the previous one
@@ -335,6 +356,45 @@ __device__ __forceinline__ void vector_phase(WaveState& w, float scale_log2, boo
   w.l_run += ps0 + ps1;
 }
 
+// The barrier between two phases; no instruction moves across it (the compiler would
+// otherwise move matrix products, which touch no memory, into the neighbouring phase).
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// One tile iteration j in the steady state (j >= 1, j + NAHEAD < n, tile j + NAHEAD
+// wholly in the context): every copy takes the scalar path from the running bases kp, vp
+// (advanced by one tile), no key is masked, and both wave groups run the same waits.
+// After the matrix phase 5 tiles of copies may stay outstanding behind tile j+1 (group 0
+// needs tile j+1 at the coming barrier, group 1 needed it one barrier earlier); after the
+// vector phase 4 behind tile j+2 (group 1 needs it at the coming barrier, group 0 waits
+// for it half an iteration early). With U >= 0 (the stage of tile j, known at compile
+// time) every LDS operand read is a lane register plus an immediate offset.
+template <int U>
+__device__ __forceinline__ void steady_iter(int j, const char*& kp, const char*& vp, size_t tstep,
+                                            uint32_t voff, uint32_t wrow, const LaneOffsets& lo,
+                                            bf16x8 (&ka)[NDS], bf16x8 (&va)[NVO],
+                                            const bf16x8 (&qreg)[NDS], WaveState& ws,
+                                            float scale_log2) {
+  const int s0 = U >= 0 ? U : (j & (NSTAGE - 1));
+  const int s1 = (s0 + 1) & (NSTAGE - 1), sa = (s0 + NAHEAD) & (NSTAGE - 1);
+  dma16u(kp, voff, (uint32_t)(uintptr_t)kst(sa) + wrow);
+  dma16u(vp, voff, (uint32_t)(uintptr_t)vst(sa) + wrow);
+  kp += tstep;
+  vp += tstep;
+  matrix_phase(ka, va, qreg, ws, true, true);
+  TT_WAIT_VM((NAHEAD - 1) * DMA_PER_TILE);
+  phase_barrier();
+  load_k_ops(kst(s1), lo, ka);
+  load_v_ops(kst(s0), lo, va);
+  __builtin_amdgcn_sched_barrier(0);
+  vector_phase(ws, scale_log2, false, 0);
+  TT_WAIT_VM((NAHEAD - 2) * DMA_PER_TILE);
+  phase_barrier();
+}
+
 // Partial slot of one (cluster, segment, query slice): O/l as bf16 [RWG][D], then m, l fp32.
 constexpr size_t kPartBytes = (size_t)RWG * D * 2 + (size_t)RWG * 8;
 
@@ -349,7 +409,7 @@ __device__ __forceinline__ size_t qrow_bytes(const AttnArgs& a, int b, int g, in
 }
 
 __global__ __launch_bounds__(NTHR, 1) void attn_mfma_kernel(AttnArgs a) {
-  __shared__ int wsum[NW];
+  int* wsum = reinterpret_cast<int*>(g_ring + NSTAGE * STAGEB);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -399,7 +459,10 @@ __global__ __launch_bounds__(NTHR, 1) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
         const int c = 4 * db + 2 * grp2 + ((j & 3) >> 1);
-        lo.v[db][h] = row * ROWB + ((c ^ fv) << 4) + (j & 1) * 8;
+        lo.v[db][h] = VOFF + row * ROWB + ((c ^ fv) << 4) + (j & 1) * 8;
+        // opaque, so that the compiler keeps VOFF in the register rather than in the
+        // reads' offset field (which holds 16 bits)
+        asm volatile("" : "+v"(lo.v[db][h]));
       }
     }
   }
@@ -445,14 +508,13 @@ __global__ __launch_bounds__(NTHR, 1) void attn_mfma_kernel(AttnArgs a) {
     src.kb = static_cast<const char*>(a.k_blk) + ((size_t)bcur * S * a.Hkv + g) * D * 2;
     src.vb = static_cast<const char*>(a.v_blk) + ((size_t)bcur * S * a.Hkv + g) * D * 2;
     src.nctx = nctx;
-    auto stage = [&](int k) { return g_ring + (k & (NSTAGE - 1)) * STAGEB; };  // local tile k
 
     // ---- prologue. Query rows of this wave -> its 8 KB behind the first NPRO stages (row
     // j of the wave at LDS row j, chunks permuted like the key tiles); row r of the unit is
     // (head-in-group r / S, position r % S); rows past the unit read its row 0 (results
     // discarded).
     const int row0 = qs * RWG + wave * RPW;  // this wave's first unit row
-    char* qst = g_ring + NPRO * STAGEB + wave * RPW * ROWB;
+    char* qst = g_ring + (wave >> 2) * VOFF + NPRO * TB + (wave & 3) * TB;
 #pragma unroll
     for (int i = 0; i < DMA_Q; ++i) {
       const int j = 4 * i + (ln >> 4);
@@ -461,7 +523,7 @@ __global__ __launch_bounds__(NTHR, 1) void attn_mfma_kernel(AttnArgs a) {
       dma16(Qb + qrow_bytes(a, bcur, g, r < rows_unit ? r : 0) + (c << 4), lds_addr(qst + 4 * i * ROWB));
     }
     const int npro = min(n, NPRO);
-    for (int k = 0; k < npro; ++k) issue_tile(src, ta + k, stage(k));
+    for (int k = 0; k < npro; ++k) issue_tile(src, ta + k, k);
     switch (npro) {  // this wave's query rows have landed
       case 1: TT_WAIT_VM(1 * DMA_PER_TILE); break;
       case 2: TT_WAIT_VM(2 * DMA_PER_TILE); break;
@@ -473,7 +535,7 @@ __global__ __launch_bounds__(NTHR, 1) void attn_mfma_kernel(AttnArgs a) {
     for (int ds = 0; ds < NDS; ++ds) qreg[ds] = ld_k(qst + lo.k[ds]);
     TT_WAIT_LGKM0();
     __syncthreads();  // every wave has its query rows: their stages take tiles now
-    for (int k = NPRO; k < min(n, NAHEAD); ++k) issue_tile(src, ta + k, stage(k));
+    for (int k = NPRO; k < min(n, NAHEAD); ++k) issue_tile(src, ta + k, k);
     wait_tiles_after(__builtin_amdgcn_readfirstlane(min(n, NAHEAD) - 1));  // local tile 0
     __syncthreads();
 
@@ -495,25 +557,49 @@ __global__ __launch_bounds__(NTHR, 1) void attn_mfma_kernel(AttnArgs a) {
     // each wave waits for its own copies of that tile (group 0 after matrix phase j, group
     // 1 after vector phase j-1). A wave issues its copies of tile j+6 at the start of its
     // matrix phase j, into the stage of tile j-2, whose last reads (vector phase j-2) both
-    // groups finished two barriers earlier.
+    // groups finished two barriers earlier. Local tile k uses stage k % 8. The first
+    // iteration, the last ones and those whose copies need the block rows take the general
+    // path below; the rest run steady_iter, eight at a time with compile-time stages.
     bf16x8 ka[NDS], va[NVO];
-    load_k_ops(stage(0), lo, ka);
+    load_k_ops(kst(0), lo, ka);
     if (grp == 1) {
       if (1 < n) wait_tiles_after(__builtin_amdgcn_readfirstlane(min(NAHEAD - 2, n - 2)));
       __syncthreads();
     }
-    for (int j = 0; j <= n; ++j) {
-      if (j + NAHEAD < n) issue_tile(src, ta + j + NAHEAD, stage(j + NAHEAD));
+    auto general_iter = [&](int j) {
+      if (j + NAHEAD < n) issue_tile(src, ta + j + NAHEAD, (j + NAHEAD) & (NSTAGE - 1));
       matrix_phase(ka, va, qreg, ws, j < n, j >= 1);
       if (grp == 0 && j + 1 < n) wait_tiles_after(__builtin_amdgcn_readfirstlane(min(NAHEAD - 1, n - 2 - j)));
-      __syncthreads();
-      if (j + 1 < n) load_k_ops(stage(j + 1), lo, ka);
-      if (j < n) load_v_ops(stage(j), lo, va);
+      phase_barrier();
+      if (j + 1 < n) load_k_ops(kst((j + 1) & (NSTAGE - 1)), lo, ka);
+      if (j < n) load_v_ops(kst(j & (NSTAGE - 1)), lo, va);
       __builtin_amdgcn_sched_barrier(0);
       if (j < n) vector_phase(ws, scale_log2, ta + j == nt - 1, nvalid - (ta + j) * KT - 4 * lh);
       if (grp == 1 && j + 2 < n) wait_tiles_after(__builtin_amdgcn_readfirstlane(min(NAHEAD - 2, n - 3 - j)));
-      __syncthreads();
+      phase_barrier();
+    };
+    general_iter(0);
+    int j = 1;
+    // last steady iteration: its copies (tile ta + j + NAHEAD) lie wholly in the context
+    const int jss = __builtin_amdgcn_readfirstlane(min(n - NAHEAD - 1, nctx / KT - ta - NAHEAD - 1));
+    if (j <= jss) {
+      const size_t tstep = (size_t)KT * src.rs;
+      const char* kp = uniform_ptr(src.kc + (size_t)(ta + 1 + NAHEAD) * tstep);
+      const char* vp = uniform_ptr(src.vc + (size_t)(ta + 1 + NAHEAD) * tstep);
+      const uint32_t wrow = __builtin_amdgcn_readfirstlane(4 * wave * ROWB);
+      for (; j + 7 <= jss; j += 8) {  // j % 8 == 1
+        steady_iter<1>(j, kp, vp, tstep, src.voff, wrow, lo, ka, va, qreg, ws, scale_log2);
+        steady_iter<2>(j + 1, kp, vp, tstep, src.voff, wrow, lo, ka, va, qreg, ws, scale_log2);
+        steady_iter<3>(j + 2, kp, vp, tstep, src.voff, wrow, lo, ka, va, qreg, ws, scale_log2);
+        steady_iter<4>(j + 3, kp, vp, tstep, src.voff, wrow, lo, ka, va, qreg, ws, scale_log2);
+        steady_iter<5>(j + 4, kp, vp, tstep, src.voff, wrow, lo, ka, va, qreg, ws, scale_log2);
+        steady_iter<6>(j + 5, kp, vp, tstep, src.voff, wrow, lo, ka, va, qreg, ws, scale_log2);
+        steady_iter<7>(j + 6, kp, vp, tstep, src.voff, wrow, lo, ka, va, qreg, ws, scale_log2);
+        steady_iter<0>(j + 7, kp, vp, tstep, src.voff, wrow, lo, ka, va, qreg, ws, scale_log2);
+      }
+      for (; j <= jss; ++j) steady_iter<-1>(j, kp, vp, tstep, src.voff, wrow, lo, ka, va, qreg, ws, scale_log2);
     }
+    for (; j <= n; ++j) general_iter(j);
     if (grp == 0) __syncthreads();
 
     // ---- epilogue: O / l as bf16 through this wave's LDS staging rows, then whole rows

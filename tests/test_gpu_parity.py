@@ -78,6 +78,8 @@ ATTN_CASES = [
     ("mfma-ctx0", 2, 16, 32, 2, 128, [0, 0], 0, W.BF16),
     ("mfma-G1", 2, 16, 4, 4, 128, [130, 7], 130, W.BF16),
     ("mfma-long-split", 1, 16, 32, 2, 128, [9000], 9000, W.BF16),
+    # segments of many lengths: every remainder of the eight-tile steady-state unrolling
+    ("mfma-steady-mix", 8, 16, 32, 2, 128, [230, 262, 295, 330, 361, 390, 425, 470], 480, W.BF16),
     ("generic-f32-cfg1", 1, 16, 4, 1, 64, [128], 128, W.F32),
     ("generic-bf16-D64", 2, 8, 8, 2, 64, [40, 300], 300, W.BF16),
     ("generic-f32-D80", 2, 3, 6, 3, 80, [0, 257], 260, W.F32),
