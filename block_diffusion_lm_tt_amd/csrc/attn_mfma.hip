@@ -14,8 +14,11 @@
 //    NQ workgroups (a "cluster") placed on one XCD so that its key stream is fetched from
 //    HBM once and shared through that XCD's L2.
 //  * Keys of a unit are the concatenation [context ; block]; the key sequence is cut in
-//    32-key tiles. All tiles of all units form one global list that is split evenly over
-//    the clusters of a persistent grid (the plan is computed in-kernel from ctx_len).
+//    32-key tiles. All units form one global list of positions, each unit a fixed number
+//    of overhead positions (the cost of a segment, in tiles) followed by its tiles; the
+//    list is split evenly over the clusters of a persistent grid (the plan is computed
+//    in-kernel from ctx_len), so a cluster's tiles plus its segments' fixed costs are
+//    about the same for every cluster.
 //    A cluster range that covers a whole unit writes the final output; a unit cut by a
 //    range boundary leaves per-piece partials (running max and sum in fp32, normalised O
 //    in bf16) that the combine kernel merges with a log-sum-exp rescale.
@@ -102,6 +105,16 @@ __device__ __forceinline__ char* vst(int s) { return g_ring + VOFF + s * TB; }
 
 __device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 
+// The lane id, recomputed where it is used (v_mbcnt, in an asm block that the compiler
+// neither hoists nor merges), so that no register holds it across the tile loop: every
+// register there is taken, and a value spilled to scratch would be reloaded behind a wait
+// for all vector-memory operations, i.e. for every tile copy in flight.
+__device__ __forceinline__ int fresh_lane() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 __device__ __forceinline__ float lane_pair_max(float v) {
   // lanes l and l^32 hold the same query column; the swap hands each lane both halves
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -128,7 +141,8 @@ __device__ __forceinline__ int clamp_ctx_u(const int32_t* ctx_len, int b, int Lm
   return n < 0 ? 0 : (n > Lmax ? Lmax : n);
 }
 
-// Exclusive prefix sums over sequences of (tiles per unit * Hkv) into P[0..B]; P[B] = total.
+// Exclusive prefix sums over sequences of (positions per unit * Hkv) into P[0..B]; P[B] =
+// total. A unit's positions: kAttnSegmentCost overhead positions, then its tiles.
 __device__ void build_plan(int* P, int* wsum, const int32_t* ctx_len, int B, int S, int Hkv,
                            int Lmax) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -137,7 +151,7 @@ __device__ void build_plan(int* P, int* wsum, const int32_t* ctx_len, int B, int
   int local = 0;
   for (int k = 0; k < per; ++k) {
     const int b = b0 + k;
-    if (b < B) local += ((clamp_ctx(ctx_len, b, Lmax) + S + KT - 1) / KT) * Hkv;
+    if (b < B) local += ((clamp_ctx(ctx_len, b, Lmax) + S + KT - 1) / KT + kAttnSegmentCost) * Hkv;
   }
   int x = local;
   for (int off = 1; off < 64; off <<= 1) {
@@ -156,7 +170,7 @@ __device__ void build_plan(int* P, int* wsum, const int32_t* ctx_len, int B, int
     const int b = b0 + k;
     if (b < B) {
       P[b] = run;
-      run += ((clamp_ctx(ctx_len, b, Lmax) + S + KT - 1) / KT) * Hkv;
+      run += ((clamp_ctx(ctx_len, b, Lmax) + S + KT - 1) / KT + kAttnSegmentCost) * Hkv;
     }
   }
   if (tid == 0) P[B] = total;
@@ -211,8 +225,7 @@ __device__ __forceinline__ uint32_t lds_addr(const char* p) {
 // Issue this wave's copies of tile t into stage st: key j < ctx_len reads context row j,
 // else block row j - ctx_len; keys past ctx_len + S read the last block row (finite data
 // whose scores are masked). One wave-uniform LDS destination per copy (1 KB = 4 rows).
-__device__ __forceinline__ void issue_tile(const TileSrc& s, int t, int st) {
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+__device__ __forceinline__ void issue_tile(const TileSrc& s, int t, int st, int w) {
   const uint32_t ldk = lds_addr(kst(st) + 4 * w * ROWB), ldv = ldk + VOFF;
   if ((t + 1) * KT <= __builtin_amdgcn_readfirstlane(s.nctx)) {
     // every key in the context: scalar bases, fixed lane offsets
@@ -221,7 +234,7 @@ __device__ __forceinline__ void issue_tile(const TileSrc& s, int t, int st) {
     dma16s(s.vc + toff, s.voff, ldv);
     return;
   }
-  const int key = t * KT + 4 * w + (lane >> 4);
+  const int key = t * KT + 4 * w + (fresh_lane() >> 4);
   const bool in_ctx = key < s.nctx;
   const int idx = in_ctx ? key : min(key - s.nctx, s.S - 1);
   const size_t off = (size_t)idx * s.rs + s.coff;
@@ -316,9 +329,9 @@ __device__ __forceinline__ void matrix_phase(const bf16x8 (&ka)[NDS], const bf16
 // Vector phase of a tile: key mask (the unit's last tile only), row max, lazy rescale,
 // P = exp2(s * scale_log2 - m) packed as the PV B operand (key-step ks = k / 8 holds
 // the values k % 8), and the row sums of the bf16-rounded P.
-__device__ __forceinline__ void vector_phase(WaveState& w, float scale_log2, bool mask, int lim) {
-  if (mask) {  // keys at or past nvalid get -inf; lim is opaque so the compares stay here
-    asm volatile("" : "+v"(lim));
+__device__ __forceinline__ void vector_phase(WaveState& w, float scale_log2, bool mask, int lim0) {
+  if (mask) {  // keys at or past nvalid get -inf (lim0: nvalid - the tile's first key)
+    const int lim = lim0 - 4 * (fresh_lane() >> 5);
 #pragma unroll
     for (int k = 0; k < 16; ++k)
       if (8 * (k >> 2) + (k & 3) >= lim) w.s[k] = -INFINITY;
@@ -420,7 +433,7 @@ __global__ __launch_bounds__(NTHR, 1) void attn_mfma_kernel(AttnArgs a) {
   const int cluster = (kk / a.NQ) * 8 + xcd;
   const int qs = kk % a.NQ;
 
-  // ---- plan: tile prefix sums in LDS, then this cluster's range of the global tile list
+  // ---- plan: position prefix sums in LDS, then this cluster's range of the global list
   int* P = reinterpret_cast<int*>(g_ring);
   build_plan(P, wsum, a.ctx_len, a.B, a.S, a.Hkv, a.Lmax);
   const int T = __builtin_amdgcn_readfirstlane(P[a.B]);
@@ -476,32 +489,29 @@ __global__ __launch_bounds__(NTHR, 1) void attn_mfma_kernel(AttnArgs a) {
   }
   const float scale_log2 = a.scale_log2;
 
-  int t = t0;
+  constexpr int SC = kAttnSegmentCost;
+  int t = t0;  // a position of the global list
   bool first_seg = true;
   int nctx = clamp_ctx_u(a.ctx_len, bcur, a.Lmax);
-  int nt = (nctx + S + KT - 1) / KT;
+  int nt = (nctx + S + KT - 1) / KT;  // tiles per unit of sequence bcur
   while (t < t1) {
-    while (t >= pb + nt * a.Hkv) {  // advance to the sequence holding tile t
-      pb = __builtin_amdgcn_readfirstlane(pb + nt * a.Hkv);
+    while (t >= pb + (nt + SC) * a.Hkv) {  // advance to the sequence holding position t
+      pb = __builtin_amdgcn_readfirstlane(pb + (nt + SC) * a.Hkv);
       bcur = __builtin_amdgcn_readfirstlane(bcur + 1);
       nctx = clamp_ctx_u(a.ctx_len, bcur, a.Lmax);
       nt = __builtin_amdgcn_readfirstlane((nctx + S + KT - 1) / KT);
     }
-    const int g = __builtin_amdgcn_readfirstlane((t - pb) / nt);
-    const int ta = __builtin_amdgcn_readfirstlane((t - pb) - g * nt);  // first local tile
-    const int ustart = pb + g * nt;
-    const int te = __builtin_amdgcn_readfirstlane(min(nt, t1 - ustart));  // one past the last
+    const int g = __builtin_amdgcn_readfirstlane((t - pb) / (nt + SC));
+    const int ustart = pb + g * (nt + SC);  // the unit's overhead positions, then its tiles
+    const int ta = __builtin_amdgcn_readfirstlane(max(t - ustart - SC, 0));  // first local tile
+    const int te = __builtin_amdgcn_readfirstlane(min(nt, t1 - ustart - SC));  // one past the last
+    t = ustart + nt + SC;
+    if (te <= ta) continue;  // the range ends among the unit's overhead positions
     const bool whole = (ta == 0 && te == nt);
     const int slot = first_seg ? 0 : 1;
     first_seg = false;
-    t = ustart + te;
     const int n = te - ta;  // tiles in this segment (>= 1)
     const int nvalid = nctx + S;
-    // an opaque copy of the lane id: the per-lane addresses of the prologue and epilogue
-    // are then computed here rather than hoisted out of the segment loop and kept live
-    // (in registers the tile loop needs) across it
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
 
     src.kc = static_cast<const char*>(a.k_ctx) + ((size_t)bcur * a.Lmax * a.Hkv + g) * D * 2;
     src.vc = static_cast<const char*>(a.v_ctx) + ((size_t)bcur * a.Lmax * a.Hkv + g) * D * 2;
@@ -515,15 +525,18 @@ __global__ __launch_bounds__(NTHR, 1) void attn_mfma_kernel(AttnArgs a) {
     // discarded).
     const int row0 = qs * RWG + wave * RPW;  // this wave's first unit row
     char* qst = g_ring + (wave >> 2) * VOFF + NPRO * TB + (wave & 3) * TB;
+    uint32_t qlds = lds_addr(qst);
+    asm volatile("" : "+s"(qlds));  // computed here, not hoisted into registers
+    const int ln = fresh_lane();
 #pragma unroll
     for (int i = 0; i < DMA_Q; ++i) {
       const int j = 4 * i + (ln >> 4);
       const int r = row0 + j;
       const int c = (ln & 15) ^ swz(j & 15);
-      dma16(Qb + qrow_bytes(a, bcur, g, r < rows_unit ? r : 0) + (c << 4), lds_addr(qst + 4 * i * ROWB));
+      dma16(Qb + qrow_bytes(a, bcur, g, r < rows_unit ? r : 0) + (c << 4), qlds + 4 * i * ROWB);
     }
     const int npro = min(n, NPRO);
-    for (int k = 0; k < npro; ++k) issue_tile(src, ta + k, k);
+    for (int k = 0; k < npro; ++k) issue_tile(src, ta + k, k, wave);
     switch (npro) {  // this wave's query rows have landed
       case 1: TT_WAIT_VM(1 * DMA_PER_TILE); break;
       case 2: TT_WAIT_VM(2 * DMA_PER_TILE); break;
@@ -535,7 +548,7 @@ __global__ __launch_bounds__(NTHR, 1) void attn_mfma_kernel(AttnArgs a) {
     for (int ds = 0; ds < NDS; ++ds) qreg[ds] = ld_k(qst + lo.k[ds]);
     TT_WAIT_LGKM0();
     __syncthreads();  // every wave has its query rows: their stages take tiles now
-    for (int k = NPRO; k < min(n, NAHEAD); ++k) issue_tile(src, ta + k, k);
+    for (int k = NPRO; k < min(n, NAHEAD); ++k) issue_tile(src, ta + k, k, wave);
     wait_tiles_after(__builtin_amdgcn_readfirstlane(min(n, NAHEAD) - 1));  // local tile 0
     __syncthreads();
 
@@ -567,14 +580,14 @@ __global__ __launch_bounds__(NTHR, 1) void attn_mfma_kernel(AttnArgs a) {
       __syncthreads();
     }
     auto general_iter = [&](int j) {
-      if (j + NAHEAD < n) issue_tile(src, ta + j + NAHEAD, (j + NAHEAD) & (NSTAGE - 1));
+      if (j + NAHEAD < n) issue_tile(src, ta + j + NAHEAD, (j + NAHEAD) & (NSTAGE - 1), wave);
       matrix_phase(ka, va, qreg, ws, j < n, j >= 1);
       if (grp == 0 && j + 1 < n) wait_tiles_after(__builtin_amdgcn_readfirstlane(min(NAHEAD - 1, n - 2 - j)));
       phase_barrier();
       if (j + 1 < n) load_k_ops(kst((j + 1) & (NSTAGE - 1)), lo, ka);
       if (j < n) load_v_ops(kst(j & (NSTAGE - 1)), lo, va);
       __builtin_amdgcn_sched_barrier(0);
-      if (j < n) vector_phase(ws, scale_log2, ta + j == nt - 1, nvalid - (ta + j) * KT - 4 * lh);
+      if (j < n) vector_phase(ws, scale_log2, ta + j == nt - 1, nvalid - (ta + j) * KT);
       if (grp == 1 && j + 2 < n) wait_tiles_after(__builtin_amdgcn_readfirstlane(min(NAHEAD - 2, n - 3 - j)));
       phase_barrier();
     };
@@ -605,10 +618,11 @@ __global__ __launch_bounds__(NTHR, 1) void attn_mfma_kernel(AttnArgs a) {
     // ---- epilogue: O / l as bf16 through this wave's LDS staging rows, then whole rows
     // to the output, or to a partial slot with m and l
     char* ost = g_ring + wave * RPW * OROWB;
+    const int ln2 = fresh_lane();
     {
       const float lt = lane_pair_sum(ws.l_run);
       const float inv = 1.0f / lt;
-      char* orow = ost + (ln & 31) * OROWB;
+      char* orow = ost + (ln2 & 31) * OROWB;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -616,11 +630,11 @@ __global__ __launch_bounds__(NTHR, 1) void attn_mfma_kernel(AttnArgs a) {
           bf16x4 v;
 #pragma unroll
           for (int k = 0; k < 4; ++k) v[k] = (__bf16)(ws.oacc[db][q4 * 4 + k] * inv);
-          *reinterpret_cast<u32x2*>(orow + (db * 32 + 8 * q4 + 4 * (ln >> 5)) * 2) = __builtin_bit_cast(u32x2, v);
+          *reinterpret_cast<u32x2*>(orow + (db * 32 + 8 * q4 + 4 * (ln2 >> 5)) * 2) = __builtin_bit_cast(u32x2, v);
         }
-      if (!whole && ln < 32) {
+      if (!whole && ln2 < 32) {
         float* ml = reinterpret_cast<float*>(part_slot(a, cluster, slot, qs) + (size_t)RWG * D * 2);
-        const int rw = wave * RPW + ln;
+        const int rw = wave * RPW + ln2;
         ml[rw] = ws.m_run;
         ml[RWG + rw] = lt;
       }
@@ -629,13 +643,13 @@ __global__ __launch_bounds__(NTHR, 1) void attn_mfma_kernel(AttnArgs a) {
     char* pbase = whole ? nullptr : part_slot(a, cluster, slot, qs) + (size_t)wave * RPW * ROWB;
 #pragma unroll 4
     for (int i = 0; i < RPW / 4; ++i) {
-      const int j = 4 * i + (ln >> 4);
-      const u32x4 v = *reinterpret_cast<const u32x4*>(ost + j * OROWB + (ln & 15) * 16);
+      const int j = 4 * i + (ln2 >> 4);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(ost + j * OROWB + (ln2 & 15) * 16);
       if (whole) {
         const int r = row0 + j;
-        if (r < rows_unit) *reinterpret_cast<u32x4*>(Ob + qrow_bytes(a, bcur, g, r) + (ln & 15) * 16) = v;
+        if (r < rows_unit) *reinterpret_cast<u32x4*>(Ob + qrow_bytes(a, bcur, g, r) + (ln2 & 15) * 16) = v;
       } else {
-        *reinterpret_cast<u32x4*>(pbase + (size_t)j * ROWB + (ln & 15) * 16) = v;
+        *reinterpret_cast<u32x4*>(pbase + (size_t)j * ROWB + (ln2 & 15) * 16) = v;
       }
     }
     __syncthreads();  // the staging rows are ring stages of the next segment
@@ -656,17 +670,18 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const c_i32* plan = (c_i32*)(uintptr_t)a.plan;
   const int T = plan[a.B];
   const int pb = plan[b];
-  const int nt = (plan[b + 1] - pb) / a.Hkv;
-  const int start = pb + g * nt, end = start + nt;
-  // cluster c owns [c*T/NC, (c+1)*T/NC); the one holding tile x is ceil((x+1)*NC/T) - 1
+  const int nu = (plan[b + 1] - pb) / a.Hkv;  // positions per unit: overhead, then tiles
+  const int ustart = pb + g * nu;
+  const int start = ustart + kAttnSegmentCost, end = ustart + nu;  // the unit's tiles
+  // cluster c owns [c*T/NC, (c+1)*T/NC); the one holding position x is ceil((x+1)*NC/T) - 1
   const int c_first = (int)((((long long)start + 1) * a.NC + T - 1) / T) - 1;
   const int c_last = (int)((((long long)end) * a.NC + T - 1) / T) - 1;
   if (c_first == c_last) return;  // one cluster saw the whole unit and wrote it already
   if (r >= rows_unit) return;
   // the first piece is its cluster's second segment when that cluster's range starts
-  // before the unit; every later piece is its cluster's first segment. With T >= NC no
-  // cluster range is empty.
-  const int first_slot = (int)(((long long)c_first * T) / a.NC) < start ? 1 : 0;
+  // before the unit (position ustart - 1 is the previous unit's last tile); every later
+  // piece is its cluster's first segment. With T >= NC no cluster range is empty.
+  const int first_slot = (int)(((long long)c_first * T) / a.NC) < ustart ? 1 : 0;
   const bool may_be_empty = T < a.NC;
   const int qsl = r / RWG, rw = r - qsl * RWG;
   float M = -INFINITY, L = 0.0f, o[8];

@@ -20,6 +20,11 @@ constexpr int kAttnRowsPerWave = 32;   // query rows (head-in-group x block posi
 constexpr int kAttnRowsPerWg = kAttnWaves * kAttnRowsPerWave;
 constexpr int kAttnMfmaD = 128;        // head dim of the MFMA kernel
 constexpr int kMaxB = 8191;            // largest batch (the tile plan sits in LDS)
+// The fixed cost of one segment (a cluster's run over one unit: query rows in, pipeline
+// fill and drain, output rows out), in tiles. The tile list is split over the clusters
+// with this many extra positions in front of each unit, so that a cluster that handles
+// more segments gets fewer tiles.
+constexpr int kAttnSegmentCost = 12;
 
 struct AttnArgs {
   const void* q;
@@ -30,10 +35,10 @@ struct AttnArgs {
   const int32_t* ctx_len;
   void* o;
   float* part;        // partial results per (cluster, segment, query slice)
-  int32_t* plan;      // [B+1] tile prefix sums, written by workgroup 0 for the combine
+  int32_t* plan;      // [B+1] position prefix sums, written by workgroup 0 for the combine
   int B, S, Hq, Hkv, G, D, Lmax;
   int NQ;             // workgroups (query slices) per (sequence, KV head) unit
-  int NC;             // clusters; each owns a contiguous range of the global tile list
+  int NC;             // clusters; each owns a contiguous range of the global position list
   float scale_log2;   // log2(e) / sqrt(D)
 };
 
