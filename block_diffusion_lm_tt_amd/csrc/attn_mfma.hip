@@ -21,7 +21,9 @@
 //    about the same for every cluster.
 //    A cluster range that covers a whole unit writes the final output; a unit cut by a
 //    range boundary leaves per-piece partials (running max and sum in fp32, normalised O
-//    in bf16) that the combine kernel merges with a log-sum-exp rescale.
+//    in bf16) that the combine kernel merges with a log-sum-exp rescale. The cluster that
+//    holds a cut unit's last piece leaves a record of the unit for the combine kernel,
+//    which then touches nothing else.
 //  * K and V tiles go HBM -> LDS directly (global_load_lds_dwordx4, no staging registers)
 //    into a ring of 8 stages of 16 KB (8 KB of keys + 8 KB of values): six tiles are in
 //    flight per CU while two are in use; explicit vmcnt waits and one barrier per tile.
@@ -421,6 +423,18 @@ __device__ __forceinline__ size_t qrow_bytes(const AttnArgs& a, int b, int g, in
   return ((((size_t)b * a.S + pos) * a.Hq + (size_t)g * a.G + hl) * D) * 2;
 }
 
+// Cluster c owns positions [range_start(c), range_start(c+1)), range_start(c) =
+// floor(c T / NC); cluster_of(x) is the one holding position x, ceil((x+1) NC / T) - 1.
+// In double: the products are integers below 2^53 (exact) and a quotient that is not an
+// integer is at least 1/max(T, NC) from one, far above the rounding error, so the floor
+// and ceil are exact.
+__device__ __forceinline__ int range_start(int c, int T, int NC) {
+  return (int)floor((double)c * (double)T / (double)NC);
+}
+__device__ __forceinline__ int cluster_of(int x, int T, int NC) {
+  return (int)ceil((double)(x + 1) * (double)NC / (double)T) - 1;
+}
+
 __global__ __launch_bounds__(NTHR, 1) void attn_mfma_kernel(AttnArgs a) {
   int* wsum = reinterpret_cast<int*>(g_ring + NSTAGE * STAGEB);
 
@@ -430,17 +444,15 @@ __global__ __launch_bounds__(NTHR, 1) void attn_mfma_kernel(AttnArgs a) {
   const int lr = lane & 31, lh = lane >> 5;
   const int id = blockIdx.x;
   const int xcd = id & 7, kk = id >> 3;
-  const int cluster = (kk / a.NQ) * 8 + xcd;
-  const int qs = kk % a.NQ;
+  const int cluster = __builtin_amdgcn_readfirstlane((kk / a.NQ) * 8 + xcd);
+  const int qs = __builtin_amdgcn_readfirstlane(kk % a.NQ);
 
   // ---- plan: position prefix sums in LDS, then this cluster's range of the global list
   int* P = reinterpret_cast<int*>(g_ring);
   build_plan(P, wsum, a.ctx_len, a.B, a.S, a.Hkv, a.Lmax);
   const int T = __builtin_amdgcn_readfirstlane(P[a.B]);
-  if (id == 0)
-    for (int b = tid; b <= a.B; b += NTHR) a.plan[b] = P[b];
-  const int t0 = (int)(((long long)cluster * T) / a.NC);
-  const int t1 = (int)(((long long)(cluster + 1) * T) / a.NC);
+  const int t0 = range_start(cluster, T, a.NC);
+  const int t1 = range_start(cluster + 1, T, a.NC);
   int bcur = 0;
   {
     int lo = 0, hi = a.B - 1;  // largest b with P[b] <= t0
@@ -453,6 +465,9 @@ __global__ __launch_bounds__(NTHR, 1) void attn_mfma_kernel(AttnArgs a) {
   int pb = __builtin_amdgcn_readfirstlane(P[bcur]);
   bcur = __builtin_amdgcn_readfirstlane(bcur);
   __syncthreads();  // P lives in the ring; done with it
+  // merge record of this cluster: none, unless its first segment is the last piece of a
+  // cut unit (written again there, by the same thread)
+  if (qs == 0 && tid == 0) *reinterpret_cast<int4*>(a.rec + 4 * cluster) = int4{-1, 0, 0, T};
   if (t0 >= t1) return;
 
   const char* Qb = static_cast<const char*>(a.q);
@@ -509,6 +524,13 @@ __global__ __launch_bounds__(NTHR, 1) void attn_mfma_kernel(AttnArgs a) {
     if (te <= ta) continue;  // the range ends among the unit's overhead positions
     const bool whole = (ta == 0 && te == nt);
     const int slot = first_seg ? 0 : 1;
+    if (first_seg && ta > 0 && te == nt && qs == 0 && wave == 0 && fresh_lane() == 0) {  // last piece of a cut unit
+      const int cf = cluster_of(ustart + SC, T, a.NC);
+      const int cs = 2 * cf + (range_start(cf, T, a.NC) < ustart ? 1 : 0);
+      int cl = __builtin_amdgcn_readfirstlane(cluster);
+      asm volatile("" : "+s"(cl));  // the address is formed here, not kept across the loop
+      *reinterpret_cast<int4*>(a.rec + 4 * cl) = int4{bcur, g, cs, T};
+    }
     first_seg = false;
     const int n = te - ta;  // tiles in this segment (>= 1)
     const int nvalid = nctx + S;
@@ -656,32 +678,25 @@ __global__ __launch_bounds__(NTHR, 1) void attn_mfma_kernel(AttnArgs a) {
   }
 }
 
-// Merge the partials of every unit that a cluster boundary cut. One workgroup covers 16
-// query rows of one unit (16 threads x 8 head-dim values per row). The pieces are read
-// eight at a time, all loads in flight together, then merged with a running max.
+// Merge the partials of every unit that a cluster boundary cut. Workgroup (c, y) reads the
+// merge record of cluster c (none: it exits) and covers 16 query rows of that unit (16
+// threads x 8 head-dim values per row). The pieces lie in clusters first .. c; they are
+// read two at a time and merged with a running max.
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
-  constexpr int PB = 8;
-  const int u = blockIdx.x;
-  const int b = u / a.Hkv, g = u - b * a.Hkv;
+  constexpr int PB = 2;  // more pieces in flight cost registers, hence occupancy: slower
+  const int c_last = blockIdx.x;
+  // the record was written by the previous kernel: scalar loads, uniform arithmetic
+  const c_i32* rec = (c_i32*)(uintptr_t)(a.rec + 4 * c_last);
+  const int b = rec[0];
+  if (b < 0) return;
+  const int g = rec[1], c_first = rec[2] >> 1, first_slot = rec[2] & 1, T = rec[3];
   const int rows_unit = a.G * a.S;
   const int r = blockIdx.y * 16 + (threadIdx.x >> 4);
-  const int d = (threadIdx.x & 15) * 8;
-  // the plan was written by the previous kernel: scalar loads, uniform arithmetic
-  const c_i32* plan = (c_i32*)(uintptr_t)a.plan;
-  const int T = plan[a.B];
-  const int pb = plan[b];
-  const int nu = (plan[b + 1] - pb) / a.Hkv;  // positions per unit: overhead, then tiles
-  const int ustart = pb + g * nu;
-  const int start = ustart + kAttnSegmentCost, end = ustart + nu;  // the unit's tiles
-  // cluster c owns [c*T/NC, (c+1)*T/NC); the one holding position x is ceil((x+1)*NC/T) - 1
-  const int c_first = (int)((((long long)start + 1) * a.NC + T - 1) / T) - 1;
-  const int c_last = (int)((((long long)end) * a.NC + T - 1) / T) - 1;
-  if (c_first == c_last) return;  // one cluster saw the whole unit and wrote it already
   if (r >= rows_unit) return;
+  const int d = (threadIdx.x & 15) * 8;
   // the first piece is its cluster's second segment when that cluster's range starts
-  // before the unit (position ustart - 1 is the previous unit's last tile); every later
-  // piece is its cluster's first segment. With T >= NC no cluster range is empty.
-  const int first_slot = (int)(((long long)c_first * T) / a.NC) < ustart ? 1 : 0;
+  // before the unit; every later piece is its cluster's first segment. With T >= NC no
+  // cluster range is empty.
   const bool may_be_empty = T < a.NC;
   const int qsl = r / RWG, rw = r - qsl * RWG;
   float M = -INFINITY, L = 0.0f, o[8];
@@ -694,8 +709,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
     for (int j = 0; j < PB; ++j) {
       const int c = c0 + j;
       bool ok = c <= c_last;
-      if (may_be_empty && ok)
-        ok = ((long long)c * T) / a.NC != ((long long)(c + 1) * T) / a.NC;
+      if (may_be_empty && ok) ok = range_start(c, T, a.NC) != range_start(c + 1, T, a.NC);
       mv[j] = -INFINITY;
       lv[j] = 0.0f;
       ov[j] = u32x4{0, 0, 0, 0};
@@ -740,7 +754,7 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s, hipEvent_t ev0, hi
   if (e != hipSuccess) return e;
   if (ev1) (void)hipEventRecord(ev1, s);
   const int rows_unit = a.G * a.S;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(a.B * a.Hkv, (rows_unit + 15) / 16), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(a.NC, (rows_unit + 15) / 16), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

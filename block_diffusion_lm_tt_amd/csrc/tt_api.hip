@@ -38,7 +38,7 @@ tt_status plan_attn(const tt_attn_shape* sh, AttnPlan* p) {
   nc = nc / 8 * 8;
   p->NC = nc < 8 ? 8 : nc;
   if (p->mfma) {
-    p->plan_bytes = align_up((size_t)(sh->B + 1) * sizeof(int32_t));
+    p->plan_bytes = align_up((size_t)p->NC * 4 * sizeof(int32_t));
     p->part_bytes = align_up(attn_part_bytes(p->NC, p->NQ));
   } else {
     p->plan_bytes = p->part_bytes = 0;
@@ -133,7 +133,7 @@ tt_status tt_block_denoise_attn(const tt_attn_shape* shape, const void* q, const
   a.v_ctx = v_ctx;
   a.ctx_len = ctx_len;
   a.o = o;
-  a.plan = static_cast<int32_t*>(workspace);
+  a.rec = static_cast<int32_t*>(workspace);
   a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.plan_bytes);
   a.B = shape->B;
   a.S = shape->S;
