@@ -95,6 +95,13 @@ static_assert(NSTAGE * TB == 65536, "immediate LDS offsets cover one tensor's st
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
+// Work-item and workgroup ids straight from the hardware registers. (The HIP accessors are
+// device-library functions; built with IEEE mode off, this file's kernels do not match
+// their attributes, so the compiler would call them rather than inline them.)
+__device__ __forceinline__ int tid_x() { return (int)__builtin_amdgcn_workitem_id_x(); }
+__device__ __forceinline__ int bid_x() { return (int)__builtin_amdgcn_workgroup_id_x(); }
+__device__ __forceinline__ int bid_y() { return (int)__builtin_amdgcn_workgroup_id_y(); }
+
 // The ring holds the K tiles of the 8 stages in its first 64 KB and the V tiles in the
 // next 64 KB, so that every LDS operand read of a stage is a fixed per-lane register plus
 // an immediate offset below 64 KB. It is the kernel's only LDS variable (at address 0);
@@ -147,7 +154,7 @@ __device__ __forceinline__ int clamp_ctx_u(const int32_t* ctx_len, int b, int Lm
 // total. A unit's positions: kAttnSegmentCost overhead positions, then its tiles.
 __device__ void build_plan(int* P, int* wsum, const int32_t* ctx_len, int B, int S, int Hkv,
                            int Lmax) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = tid_x(), lane = tid & 63, w = tid >> 6;
   const int per = (B + NTHR - 1) / NTHR;
   const int b0 = tid * per;
   int local = 0;
@@ -438,11 +445,11 @@ __device__ __forceinline__ int cluster_of(int x, int T, int NC) {
 __global__ __launch_bounds__(NTHR, 1) void attn_mfma_kernel(AttnArgs a) {
   int* wsum = reinterpret_cast<int*>(g_ring + NSTAGE * STAGEB);
 
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = tid_x(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 2;  // 0: matrix phase first, 1: vector phase first
   const int lr = lane & 31, lh = lane >> 5;
-  const int id = blockIdx.x;
+  const int id = bid_x();
   const int xcd = id & 7, kk = id >> 3;
   const int cluster = __builtin_amdgcn_readfirstlane((kk / a.NQ) * 8 + xcd);
   const int qs = __builtin_amdgcn_readfirstlane(kk % a.NQ);
@@ -468,7 +475,13 @@ __global__ __launch_bounds__(NTHR, 1) void attn_mfma_kernel(AttnArgs a) {
   // merge record of this cluster: none, unless its first segment is the last piece of a
   // cut unit (written again there, by the same thread)
   if (qs == 0 && tid == 0) *reinterpret_cast<int4*>(a.rec + 4 * cluster) = int4{-1, 0, 0, T};
-  if (t0 >= t1) return;
+  if (t0 >= t1) {
+    // an empty range (only when T < NC): its slot-0 piece is marked empty (l = 0) for the
+    // combine, which may meet it between the first and the last piece of a cut unit
+    float* ml = reinterpret_cast<float*>(part_slot(a, cluster, 0, qs) + (size_t)RWG * D * 2);
+    if (tid < RWG) ml[RWG + tid] = 0.0f;
+    return;
+  }
 
   const char* Qb = static_cast<const char*>(a.q);
   char* Ob = static_cast<char*>(a.o);
@@ -681,24 +694,27 @@ __global__ __launch_bounds__(NTHR, 1) void attn_mfma_kernel(AttnArgs a) {
 // Merge the partials of every unit that a cluster boundary cut. Workgroup (c, y) reads the
 // merge record of cluster c (none: it exits) and covers 16 query rows of that unit (16
 // threads x 8 head-dim values per row). The pieces lie in clusters first .. c; they are
-// read two at a time and merged with a running max.
+// read eight at a time, all loads in flight together, and merged with a running max.
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
-  constexpr int PB = 2;  // more pieces in flight cost registers, hence occupancy: slower
-  const int c_last = blockIdx.x;
+  constexpr int PB = 8;
+  const int c_last = bid_x();
   // the record was written by the previous kernel: scalar loads, uniform arithmetic
   const c_i32* rec = (c_i32*)(uintptr_t)(a.rec + 4 * c_last);
   const int b = rec[0];
   if (b < 0) return;
-  const int g = rec[1], c_first = rec[2] >> 1, first_slot = rec[2] & 1, T = rec[3];
+  const int g = rec[1], c_first = rec[2] >> 1, first_slot = rec[2] & 1;
   const int rows_unit = a.G * a.S;
-  const int r = blockIdx.y * 16 + (threadIdx.x >> 4);
+  const int r = bid_y() * 16 + (tid_x() >> 4);
   if (r >= rows_unit) return;
-  const int d = (threadIdx.x & 15) * 8;
-  // the first piece is its cluster's second segment when that cluster's range starts
-  // before the unit; every later piece is its cluster's first segment. With T >= NC no
-  // cluster range is empty.
-  const bool may_be_empty = T < a.NC;
+  const int d = (tid_x() & 15) * 8;
   const int qsl = r / RWG, rw = r - qsl * RWG;
+  // the first piece is its cluster's second segment when that cluster's range starts
+  // before the unit; every later piece is its cluster's first segment (l = 0 marks the
+  // piece of an empty range). Piece c + 1 lies 2 * NQ slots after piece c.
+  const size_t step = (size_t)2 * a.NQ * kPartBytes;
+  const char* p0 = part_slot(a, c_first, first_slot, qsl) + ((size_t)rw * D + d) * 2;
+  const char* q0 = part_slot(a, c_first, 0, qsl) + ((size_t)rw * D + d) * 2;  // pieces after the first
+  const int lo_off = RWG * D * 2 - (rw * D + d) * 2;  // from the O chunk to this row's m
   float M = -INFINITY, L = 0.0f, o[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) o[k] = 0.0f;
@@ -706,20 +722,13 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
     float mv[PB], lv[PB];
     u32x4 ov[PB];
 #pragma unroll
-    for (int j = 0; j < PB; ++j) {
-      const int c = c0 + j;
-      bool ok = c <= c_last;
-      if (may_be_empty && ok) ok = range_start(c, T, a.NC) != range_start(c + 1, T, a.NC);
-      mv[j] = -INFINITY;
-      lv[j] = 0.0f;
-      ov[j] = u32x4{0, 0, 0, 0};
-      if (ok) {
-        const char* base = part_slot(a, c, c == c_first ? first_slot : 0, qsl);
-        const float* ml = reinterpret_cast<const float*>(base + (size_t)RWG * D * 2);
-        mv[j] = ml[rw];
-        lv[j] = ml[RWG + rw];
-        ov[j] = *reinterpret_cast<const u32x4*>(base + ((size_t)rw * D + d) * 2);
-      }
+    for (int j = 0; j < PB; ++j) {  // unconditional loads (of the last piece past the end)
+      const int c = min(c0 + j, c_last);
+      const char* po = (c == c_first ? p0 : q0 + (size_t)(c - c_first) * step);
+      const float* ml = reinterpret_cast<const float*>(po + lo_off) + rw;
+      mv[j] = ml[0];
+      lv[j] = c0 + j <= c_last ? ml[RWG] : 0.0f;
+      ov[j] = *reinterpret_cast<const u32x4*>(po);
     }
 #pragma unroll
     for (int j = 0; j < PB; ++j) {
