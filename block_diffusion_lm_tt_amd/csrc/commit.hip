@@ -8,14 +8,16 @@
 //
 // How: the work is one pass over the masked rows' logits, so it is HBM bound. Two
 // launches, with no communication between workgroups inside a launch:
-//  1. commit_reduce: one workgroup per (masked row, vocabulary chunk). Each thread loads its
-//     chunk elements with 16-byte non-temporal loads into registers, finds its max and
-//     lowest argmax, and the workgroup merges them (wave shuffles + LDS, lowest index on
-//     ties); a second pass over the registers sums exp2((x - max) * log2 e) in fp32 per
-//     thread and fp64 across threads. Unmasked rows exit at once and are never read.
+//  1. commit_reduce: one workgroup per (masked row, vocabulary chunk). Each thread issues its
+//     eight 16-byte non-temporal loads at once and consumes them in element order with an
+//     online max, lowest argmax and sum of exp2((x - m) * log2 e) relative to its running
+//     max m (rescaled when m grows); the workgroup merges (max, argmax) (wave shuffles +
+//     LDS, lowest index on ties) and sums the threads' partials, moved to the chunk max, in
+//     fp64. Unmasked rows exit at once and are never read.
 //  2. commit_decide: one workgroup per sequence. It merges each masked row's chunks in chunk
 //     order (fp64), giving the row's token and an estimate of Z whose relative error is
-//     below 1e-5 (exp2 of an exactly formed difference, <= 64 terms per fp32 partial). A
+//     below 1e-5 (per fp32 partial: 64 terms, each exp2 of a scaled difference to the
+//     running max, and at most 9 rescalings; about 7e-6 in the worst case). A
 //     threshold decision is taken on the estimate only outside a relative band of 1e-4; the
 //     fallback is taken on the estimate only when its winner leads every other position by
 //     more than 4e-4. Positions inside a band are recomputed by the same workgroup over the
@@ -53,7 +55,6 @@ __device__ __forceinline__ void argmax_merge(float& m, int& tok, float m2, int t
 template <typename T>
 __global__ __launch_bounds__(NT) void commit_reduce_kernel(CommitArgs a) {
   constexpr int VE = Vec<T>::N;
-  constexpr int EPT = VE * LOADS;
   __shared__ float sm_m[4];
   __shared__ int sm_t[4];
   __shared__ double sm_z[4];
@@ -66,34 +67,54 @@ __global__ __launch_bounds__(NT) void commit_reduce_kernel(CommitArgs a) {
   const int begin = ch * a.chunk_elems;
   const int end = min(a.V, begin + a.chunk_elems);
 
-  float x[EPT];
+  // All of the thread's 16-byte loads are issued first; each is consumed as it lands, in
+  // increasing element order, by an online max / lowest argmax / rescaled sum (few live
+  // registers, so many workgroups per CU and many loads in flight). A chunk that is not
+  // whole (the row's last) or not 16-byte aligned takes element loads instead.
+  float m = -INFINITY, sf = 0.0f;  // sf = sum of exp2((x - m) log2 e) over the elements seen
+  int tok = 0x7fffffff;
+  auto consume = [&](const float (&v)[VE], int i0) {
+    float mb = v[0];
+    int kb = 0;
 #pragma unroll
-  for (int ld = 0; ld < LOADS; ++ld) {
-    const int i0 = begin + (ld * NT + tid) * VE;
-    const T* p = base + i0;
-    if (i0 + VE <= end && ((reinterpret_cast<uintptr_t>(p) & 15) == 0)) {
-      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-      const T* e = reinterpret_cast<const T*>(&v);
+    for (int k = 1; k < VE; ++k)
+      if (v[k] > mb) {
+        mb = v[k];
+        kb = k;
+      }
+    if (mb > m) tok = i0 + kb;  // strict: an equal later value keeps the lower index
+    const float mn = fmaxf(m, mb);
+    sf *= (m == mn) ? 1.0f : __builtin_amdgcn_exp2f((m - mn) * kLog2e);  // exp2(-inf) = 0
+    if (mn != -INFINITY) {
 #pragma unroll
-      for (int k = 0; k < VE; ++k) x[ld * VE + k] = to_f(e[k]);
-    } else {
+      for (int k = 0; k < VE; ++k) sf += __builtin_amdgcn_exp2f((v[k] - mn) * kLog2e);  // -inf -> 0
+    }
+    m = mn;
+  };
+  const bool whole = begin + a.chunk_elems <= end && ((reinterpret_cast<uintptr_t>(base + begin) & 15) == 0);
+  if (whole) {
+    u32x4 raw[LOADS];
 #pragma unroll
-      for (int k = 0; k < VE; ++k) x[ld * VE + k] = (i0 + k < end) ? to_f(p[k]) : -INFINITY;
+    for (int ld = 0; ld < LOADS; ++ld)
+      raw[ld] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + begin + (ld * NT + tid) * VE));
+#pragma unroll
+    for (int ld = 0; ld < LOADS; ++ld) {
+      const T* e = reinterpret_cast<const T*>(&raw[ld]);
+      float v[VE];
+#pragma unroll
+      for (int k = 0; k < VE; ++k) v[k] = to_f(e[k]);
+      consume(v, begin + (ld * NT + tid) * VE);
+    }
+  } else {
+    for (int ld = 0; ld < LOADS; ++ld) {
+      const int i0 = begin + (ld * NT + tid) * VE;
+      float v[VE];
+#pragma unroll
+      for (int k = 0; k < VE; ++k) v[k] = (i0 + k < end) ? to_f(base[i0 + k]) : -INFINITY;
+      consume(v, i0);
     }
   }
-  // thread max / lowest argmax (elements are visited in increasing index order)
-  float m = -INFINITY;
-  int tok = 0x7fffffff;
-#pragma unroll
-  for (int ld = 0; ld < LOADS; ++ld)
-#pragma unroll
-    for (int k = 0; k < VE; ++k) {
-      const float v = x[ld * VE + k];
-      if (v > m) {
-        m = v;
-        tok = begin + (ld * NT + tid) * VE + k;
-      }
-    }
+  const float mt = m;  // this thread's max: its sum is relative to it
   for (int off = 32; off > 0; off >>= 1) {
     const float m2 = __shfl_xor(m, off, 64);
     const int t2 = __shfl_xor(tok, off, 64);
@@ -108,9 +129,8 @@ __global__ __launch_bounds__(NT) void commit_reduce_kernel(CommitArgs a) {
   int TOK = sm_t[0];
   for (int k = 1; k < 4; ++k) argmax_merge(M, TOK, sm_m[k], sm_t[k]);
 
-  float zf = 0.0f;
-#pragma unroll
-  for (int i = 0; i < EPT; ++i) zf += __builtin_amdgcn_exp2f((x[i] - M) * kLog2e);  // -inf -> 0
+  // the thread's sum moved to the chunk max (mt <= M; a thread that saw only -inf adds 0)
+  const float zf = mt == -INFINITY ? 0.0f : sf * __builtin_amdgcn_exp2f((mt - M) * kLog2e);
   double z = (double)zf;
   for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off, 64);
   if (lane == 0) sm_z[w] = z;
