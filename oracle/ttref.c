@@ -242,3 +242,43 @@ int ttref_commit(int B, int S, int V, int dtype, const void *logits, const uint8
     }
     return TTREF_OK;
 }
+
+/*
+ * The context cache update after a block is committed ([GS] Generation Process: once a
+ * block is committed, the context tower updates its states with the new clean tokens;
+ * [SN] "Blockwise generering i praksis": the context tower then updates its caches and
+ * Mamba states, once per block). For one attention layer the block's new key and value
+ * rows k_new, v_new [B,S,Hkv,D] are written at positions ctx_len[b] .. ctx_len[b]+S-1 of
+ * that layer's cache k_ctx, v_ctx [B,Lmax,Hkv,D]; with bump != 0, ctx_len[b] then grows by
+ * S (the last layer's call of a step bumps). A sequence whose block does not fit
+ * (ctx_len[b] < 0 or ctx_len[b] + S > Lmax) is left as it is and gets skipped[b] = 1
+ * (else 0). Element bits are copied unchanged: no arithmetic.
+ */
+int ttref_ctx_append(int B, int S, int Hkv, int D, int Lmax, int dtype, const void *k_new,
+                     const void *v_new, void *k_ctx, void *v_ctx, int32_t *ctx_len, int bump,
+                     uint8_t *skipped)
+{
+    if (B < 0 || S < 1 || Hkv < 1 || D < 1 || Lmax < 0)
+        return TTREF_EINVAL;
+    if (dtype != TTREF_F32 && dtype != TTREF_BF16)
+        return TTREF_EINVAL;
+    const size_t elt = dtype == TTREF_F32 ? 4 : 2;
+    const size_t row = (size_t)Hkv * D * elt; /* bytes of one position, all KV heads */
+    for (int b = 0; b < B; ++b) {
+        const int n = ctx_len[b];
+        if (n < 0 || (long long)n + S > Lmax) {
+            skipped[b] = 1;
+            continue;
+        }
+        skipped[b] = 0;
+        for (int i = 0; i < S; ++i) {
+            const size_t src = ((size_t)b * S + i) * row;
+            const size_t dst = ((size_t)b * Lmax + n + i) * row;
+            memcpy((char *)k_ctx + dst, (const char *)k_new + src, row);
+            memcpy((char *)v_ctx + dst, (const char *)v_new + src, row);
+        }
+        if (bump)
+            ctx_len[b] = n + S;
+    }
+    return TTREF_OK;
+}

@@ -35,6 +35,8 @@ def _lib():
         L.ttref_commit.restype = i32
         L.ttref_decode.argtypes = [vp, ctypes.c_size_t, i32]
         L.ttref_decode.restype = ctypes.c_double
+        L.ttref_ctx_append.argtypes = [i32] * 6 + [vp] * 5 + [i32, vp]
+        L.ttref_ctx_append.restype = i32
         L.ttref_threads.argtypes = []
         L.ttref_threads.restype = i32
         _LIB = L
@@ -95,3 +97,21 @@ def ttref_commit(B, S, V, dtype, logits, mask, gamma):
     if rc != 0:
         raise ValueError(f"ttref_commit failed with status {rc}")
     return tok, com, conf, z
+
+
+def ttref_ctx_append(B, S, Hkv, D, Lmax, dtype, k_new, v_new, k_ctx, v_ctx, ctx_len, bump):
+    """Returns (k_ctx', v_ctx', ctx_len', skipped): updated copies of the cache and lengths,
+    and uint8[B] flags of the sequences whose block did not fit. The inputs are not modified."""
+    for t in (k_new, v_new, k_ctx, v_ctx):
+        _check_dtype(t, dtype)
+    assert k_new.size == B * S * Hkv * D and v_new.size == k_new.size
+    assert k_ctx.size == B * Lmax * Hkv * D and v_ctx.size == k_ctx.size
+    kc, vc = np.array(k_ctx, copy=True), np.array(v_ctx, copy=True)
+    ctx = np.array(ctx_len, dtype=np.int32, copy=True)
+    assert ctx.size == B
+    skipped = np.zeros(B, dtype=np.uint8)
+    rc = _lib().ttref_ctx_append(B, S, Hkv, D, Lmax, _DT[dtype], _ptr(k_new), _ptr(v_new), _ptr(kc),
+                                 _ptr(vc), _ptr(ctx), int(bool(bump)), _ptr(skipped))
+    if rc != 0:
+        raise ValueError(f"ttref_ctx_append failed with status {rc}")
+    return kc, vc, ctx, skipped

@@ -2,7 +2,8 @@
 
 Each case copies oracle/ttref.c, applies one plausible slip (a dropped scale, a flipped
 sign, a wrong KV-head index, a transposed layout, values read from K, a dropped block key,
->= instead of >, a wrong tie rule, a missing fallback), builds that copy into a temporary
+>= instead of >, a wrong tie rule, a missing fallback, a cache update at the wrong rows,
+without the length bump or with an off-by-one fit test), builds that copy into a temporary
 library and runs the pin suite against it in a child process. The suite must fail.
 """
 import os
@@ -28,6 +29,12 @@ MUTANTS = {
     "no_fallback": ("if (any_masked && !any_committed)", "if (0)"),
     "z_sign": ("z += exp(ttref_load(logits, off + v, dtype) - m);",
                "z += exp(m - ttref_load(logits, off + v, dtype));"),
+    "append_ignores_length": ("const size_t dst = ((size_t)b * Lmax + n + i) * row;",
+                              "const size_t dst = ((size_t)b * Lmax + i) * row;"),
+    "append_no_bump": ("ctx_len[b] = n + S;", "ctx_len[b] = n;"),
+    "append_fit_off_by_one": ("(long long)n + S > Lmax", "(long long)n + S >= Lmax"),
+    "append_values_from_keys": ("memcpy((char *)v_ctx + dst, (const char *)v_new + src, row);",
+                                "memcpy((char *)v_ctx + dst, (const char *)k_new + src, row);"),
 }
 
 

@@ -15,7 +15,7 @@ import scipy.special
 import torch
 
 from block_diffusion_lm_tt_amd import workloads as W
-from oracle import ttref_block_denoise_attn, ttref_commit, ttref_decode
+from oracle import ttref_block_denoise_attn, ttref_commit, ttref_ctx_append, ttref_decode
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -323,3 +323,84 @@ def test_commit_rejects_nan_gamma():
     c = W.make_commit(1, 2, 10, W.F32, seed=1)
     with pytest.raises(ValueError):
         _commit(c, float("nan"))
+
+
+
+# ---- context cache update after a commit ------------------------------------------------------
+
+def _append_case(B, S, Hkv, D, Lmax, dtype, ctx, seed):
+    rng = np.random.default_rng(seed)
+    bits = np.uint16 if dtype == W.BF16 else np.float32
+    mk = (lambda *sh: rng.integers(0, 1 << 16, size=sh, dtype=np.uint16)) if dtype == W.BF16 else \
+        (lambda *sh: rng.standard_normal(sh).astype(np.float32))
+    kn, vn = mk(B, S, Hkv, D), mk(B, S, Hkv, D)
+    kc, vc = mk(B, Lmax, Hkv, D), mk(B, Lmax, Hkv, D)
+    assert kn.dtype == bits
+    return kn, vn, kc, vc, np.array(ctx, dtype=np.int32)
+
+
+@pytest.mark.parametrize("dtype", [W.BF16, W.F32])
+def test_append_equals_concatenation(dtype):
+    """Each fitting sequence's cache is [old rows 0:n ; the block ; old rows n+S:], built here with
+    numpy concatenation; the rest is untouched and flagged."""
+    B, S, Hkv, D, Lmax = 6, 3, 2, 5, 9
+    ctx = [0, 4, 6, 7, 9, -1]  # fits, fits, fits exactly, too long, full, negative
+    kn, vn, kc, vc, cl = _append_case(B, S, Hkv, D, Lmax, dtype, ctx, seed=3)
+    k2, v2, c2, skipped = ttref_ctx_append(B, S, Hkv, D, Lmax, dtype, kn, vn, kc, vc, cl, bump=1)
+    for b, n in enumerate(ctx):
+        fits = 0 <= n and n + S <= Lmax
+        assert skipped[b] == (0 if fits else 1)
+        if fits:
+            ek = np.concatenate([kc[b, :n], kn[b], kc[b, n + S:]])
+            ev = np.concatenate([vc[b, :n], vn[b], vc[b, n + S:]])
+            assert c2[b] == n + S
+        else:
+            ek, ev = kc[b], vc[b]
+            assert c2[b] == n
+        assert ek.tobytes() == k2[b].tobytes() and ev.tobytes() == v2[b].tobytes(), f"sequence {b}"
+
+
+def test_append_without_bump_keeps_lengths():
+    kn, vn, kc, vc, cl = _append_case(3, 2, 1, 4, 8, W.BF16, [0, 3, 6], seed=4)
+    k2, _, c2, skipped = ttref_ctx_append(3, 2, 1, 4, 8, W.BF16, kn, vn, kc, vc, cl, bump=0)
+    assert np.array_equal(c2, cl) and not skipped.any()
+    assert np.array_equal(k2[1, 3:5], kn[1])
+
+
+def test_append_twice_equals_one_append_of_both_blocks():
+    """Appending block A then block B (bumping) equals appending [A ; B] as one block of 2S."""
+    B, S, Hkv, D, Lmax = 4, 3, 2, 4, 13
+    ctx = [0, 2, 7, 5]
+    ka, va, kc, vc, cl = _append_case(B, S, Hkv, D, Lmax, W.BF16, ctx, seed=5)
+    kb, vb, _, _, _ = _append_case(B, S, Hkv, D, Lmax, W.BF16, ctx, seed=6)
+    k1, v1, c1, _ = ttref_ctx_append(B, S, Hkv, D, Lmax, W.BF16, ka, va, kc, vc, cl, bump=1)
+    k1, v1, c1, s1 = ttref_ctx_append(B, S, Hkv, D, Lmax, W.BF16, kb, vb, k1, v1, c1, bump=1)
+    kab = np.ascontiguousarray(np.concatenate([ka, kb], axis=1))
+    vab = np.ascontiguousarray(np.concatenate([va, vb], axis=1))
+    k2, v2, c2, s2 = ttref_ctx_append(B, 2 * S, Hkv, D, Lmax, W.BF16, kab, vab, kc, vc, cl, bump=1)
+    assert np.array_equal(s1, s2) and np.array_equal(c1, c2)
+    assert np.array_equal(k1, k2) and np.array_equal(v1, v2)
+
+
+def test_append_then_attention_sees_the_block_as_context():
+    """After the update, attention with an empty block position set reduces to the keys
+    [old context ; appended block]: torch fp64 SDPA over that concatenation agrees with the
+    oracle attention run on the updated cache (S'=1 query block whose own key is appended too)."""
+    B, S, Hq, Hkv, D, Lmax = 2, 4, 4, 2, 8, 12
+    x = W.make_attn(B, S, Hq, Hkv, D, [3, 5], Lmax=Lmax, dtype=W.BF16, seed=7)
+    k2, v2, c2, _ = ttref_ctx_append(B, S, Hkv, D, Lmax, W.BF16, x.k_blk, x.v_blk, x.k_ctx, x.v_ctx,
+                                     x.ctx_len, bump=1)
+    y = W.AttnInputs(B, S, Hq, Hkv, D, Lmax, W.BF16, x.q, x.k_blk, x.v_blk, k2, v2, c2)
+    # keys seen by y: [ctx ; block ; block] -- the block twice. SDPA over exactly that set:
+    out = torch.zeros((B, S, Hq, D), dtype=torch.float64)
+    q = _dec(x.q, W.BF16)
+    for b in range(B):
+        n = int(c2[b])
+        keys = torch.cat([_dec(k2, W.BF16)[b, :n], _dec(x.k_blk, W.BF16)[b]], 0)
+        vals = torch.cat([_dec(v2, W.BF16)[b, :n], _dec(x.v_blk, W.BF16)[b]], 0)
+        qq = q[b].permute(1, 0, 2)                       # [Hq, S, D]
+        kk = keys.permute(1, 0, 2).repeat_interleave(Hq // Hkv, 0)
+        vv = vals.permute(1, 0, 2).repeat_interleave(Hq // Hkv, 0)
+        out[b] = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv).permute(1, 0, 2)
+    got = _attn(y)
+    assert np.abs(got - out.numpy()).max() < 1e-12
