@@ -56,6 +56,8 @@ def lib() -> ctypes.CDLL:
         L.tt_version.argtypes = []
         L.tt_status_str.restype = ctypes.c_char_p
         L.tt_status_str.argtypes = [i32]
+        L.tt_ctx_append.restype = i32
+        L.tt_ctx_append.argtypes = [ctypes.POINTER(AttnShape), vp, vp, vp, vp, vp, i32, vp, vp]
         L.tt_block_denoise_attn_workspace.restype = sz
         L.tt_block_denoise_attn_workspace.argtypes = [ctypes.POINTER(AttnShape)]
         L.tt_block_denoise_attn.restype = i32
@@ -200,6 +202,42 @@ def tt_commit(logits, mask, gamma: float, token_id=None, committed=None, conf=No
                          workspace.data_ptr(), workspace.numel(), _stream(dev, stream))
     _check("tt_commit", st)
     return token_id, committed, conf
+
+
+def tt_ctx_append(k_new, v_new, k_ctx, v_ctx, ctx_len, bump: bool = True, skipped=None,
+                  want_skipped: bool = False, stream=None):
+    """Writes the committed block's new K/V rows [B,S,Hkv,D] into the context cache at ctx_len
+    (in place) and, with bump, adds S to ctx_len (see include/tt.h). Returns the uint8[B]
+    skipped flags when requested (want_skipped or a skipped tensor given), else None."""
+    torch = _torch()
+    for name, t in (("k_new", k_new), ("v_new", v_new), ("k_ctx", k_ctx), ("v_ctx", v_ctx),
+                    ("ctx_len", ctx_len)):
+        _dev(t, name)
+    B, S, Hkv, D = k_new.shape
+    Lmax = k_ctx.shape[1]
+    if v_new.shape != k_new.shape:
+        raise ValueError("k_new/v_new must be [B,S,Hkv,D]")
+    if k_ctx.shape != (B, Lmax, Hkv, D) or v_ctx.shape != k_ctx.shape:
+        raise ValueError("k_ctx/v_ctx must be [B,Lmax,Hkv,D] matching k_new")
+    if ctx_len.dtype != torch.int32 or ctx_len.shape != (B,):
+        raise ValueError("ctx_len must be int32 [B]")
+    dt = _dtype_code(k_new)
+    for t in (v_new, k_ctx, v_ctx):
+        if t.dtype != k_new.dtype:
+            raise TypeError("k_new, v_new, k_ctx and v_ctx must share one dtype")
+    if skipped is None and want_skipped:
+        skipped = torch.empty((B,), dtype=torch.uint8, device=k_new.device)
+    if skipped is not None:
+        if skipped.dtype != torch.uint8 or skipped.shape != (B,):
+            raise ValueError("skipped must be uint8 [B]")
+        _dev(skipped, "skipped")
+    sh = attn_shape(B, S, Hkv, Hkv, D, Lmax, dt)
+    st = lib().tt_ctx_append(ctypes.byref(sh), k_new.data_ptr(), v_new.data_ptr(), k_ctx.data_ptr(),
+                             v_ctx.data_ptr(), ctx_len.data_ptr(), 1 if bump else 0,
+                             skipped.data_ptr() if skipped is not None else None,
+                             _stream(k_new.device, stream))
+    _check("tt_ctx_append", st)
+    return skipped
 
 
 def profile_enable(on: bool = True):

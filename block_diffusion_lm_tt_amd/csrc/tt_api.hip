@@ -223,6 +223,36 @@ tt_status tt_commit(int32_t B, int32_t S, int32_t V, int32_t dtype, const void* 
   return e == hipSuccess ? TT_OK : TT_ERR_HIP;
 }
 
+tt_status tt_ctx_append(const tt_attn_shape* shape, const void* k_new, const void* v_new,
+                        void* k_ctx, void* v_ctx, int32_t* ctx_len, int32_t bump, uint8_t* skipped,
+                        hipStream_t stream) {
+  if (!shape) return TT_ERR_INVALID_ARG;
+  const tt_attn_shape& sh = *shape;
+  if (sh.B < 0 || sh.S < 1 || sh.Hkv < 1 || sh.D < 1 || sh.Lmax < 0) return TT_ERR_INVALID_ARG;
+  if (sh.dtype != TT_F32 && sh.dtype != TT_BF16) return TT_ERR_UNSUPPORTED;
+  if (sh.B > kMaxB || sh.S > 1024 || sh.D > 256) return TT_ERR_UNSUPPORTED;
+  if ((long long)sh.B * sh.Lmax * sh.Hkv * sh.D >= (1LL << 31)) return TT_ERR_UNSUPPORTED;
+  if ((long long)sh.B * sh.S * sh.Hkv * sh.D >= (1LL << 31)) return TT_ERR_UNSUPPORTED;
+  if (sh.B == 0) return TT_OK;
+  if (!k_new || !v_new || !k_ctx || !v_ctx || !ctx_len) return TT_ERR_INVALID_ARG;
+  AppendArgs a;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_ctx = k_ctx;
+  a.v_ctx = v_ctx;
+  a.ctx_len = ctx_len;
+  a.skipped = skipped;
+  a.B = sh.B;
+  a.S = sh.S;
+  a.Lmax = sh.Lmax;
+  a.elt = sh.dtype == TT_F32 ? 4 : 2;
+  a.row_bytes = (size_t)sh.Hkv * sh.D * a.elt;
+  a.bump = bump != 0;
+  const uintptr_t bases = (uintptr_t)k_new | (uintptr_t)v_new | (uintptr_t)k_ctx | (uintptr_t)v_ctx;
+  a.vec16 = (a.row_bytes % 16 == 0) && (bases % 16 == 0);
+  return launch_ctx_append(a, stream) == hipSuccess ? TT_OK : TT_ERR_HIP;
+}
+
 tt_status tt_profile_enable(int32_t enable) {
   std::lock_guard<std::mutex> lk(g_prof.mu);
   g_prof.enabled = enable != 0;

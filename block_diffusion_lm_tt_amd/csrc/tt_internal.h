@@ -71,6 +71,26 @@ struct CommitArgs {
   int dtype;
 };
 
+// ---------------------------------------------------------------------------------------
+// context cache update after a commit
+// ---------------------------------------------------------------------------------------
+
+struct AppendArgs {
+  const void* k_new;
+  const void* v_new;
+  void* k_ctx;
+  void* v_ctx;
+  int32_t* ctx_len;
+  uint8_t* skipped;    // may be null
+  int B, S, Lmax;
+  size_t row_bytes;    // Hkv * D * element size
+  int elt;             // element size in bytes
+  int bump;
+  int vec16;           // every run and base 16-byte aligned
+};
+
+hipError_t launch_ctx_append(const AppendArgs& a, hipStream_t s);
+
 int commit_chunk_elems(int dtype);
 hipError_t launch_commit(const CommitArgs& a, hipStream_t s, hipEvent_t ev_reduce0, hipEvent_t ev_reduce1);
 

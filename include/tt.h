@@ -130,6 +130,36 @@ tt_status tt_commit(int32_t B, int32_t S, int32_t V, int32_t dtype, const void *
                     float *conf, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------
+ * tt_ctx_append -- context cache update after a block is committed.
+ *
+ * Defined by Nemotron-TwoTower (gist.science explainer), Technical Summary > Generation
+ * Process (once a block is committed, the context tower updates its states with the new
+ * clean tokens) and the snilld.dk TwoTower article, "Blockwise generering i praksis" (the
+ * context tower then updates its caches, once per block rather than per token). For one
+ * attention layer, the new key and value rows of the committed block (the context tower's
+ * output for its clean tokens, computed by the caller) are written after the context:
+ *
+ *   k_ctx[b, ctx_len[b] + i, :, :] = k_new[b, i, :, :]   for i < S   (likewise v)
+ *   and, when bump != 0, ctx_len[b] += S   (call with bump on the last layer of a step)
+ *
+ *   k_new, v_new  [B, S, Hkv, D]     dtype    (device, read)
+ *   k_ctx, v_ctx  [B, Lmax, Hkv, D]  dtype    (device, read and written: rows ctx_len[b] ..
+ *                                              ctx_len[b]+S-1 only)
+ *   ctx_len       [B] int32                   (device, read; written when bump != 0)
+ *   skipped       [B] uint8, may be NULL      (device, written: 1 where the block did not fit)
+ * A sequence whose block does not fit (ctx_len[b] < 0 or ctx_len[b] + S > Lmax) is left
+ * unchanged, its ctx_len included, and flagged in skipped. Element bits are copied
+ * unchanged. The shape's Hq is not used.
+ *
+ * Supported: dtype TT_BF16 or TT_F32; 1 <= S <= 1024; 1 <= D <= 256; B <= 8191;
+ * B*Lmax*Hkv*D, B*S*Hkv*D < 2^31. Anything else returns TT_ERR_UNSUPPORTED. B == 0 is a
+ * no-op. k_new/v_new must not overlap k_ctx/v_ctx/ctx_len. No workspace.
+ * ------------------------------------------------------------------------------------- */
+tt_status tt_ctx_append(const tt_attn_shape *shape, const void *k_new, const void *v_new,
+                        void *k_ctx, void *v_ctx, int32_t *ctx_len, int32_t bump,
+                        uint8_t *skipped, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------
  * Kernel timing (measurement support). While enabled, each call records HIP events on its
  * stream around the kernels listed in tt_profile_stats. The events are created once, on
  * the first enable (no device memory); up to 4096 calls per field are recorded, later ones

@@ -104,6 +104,27 @@ def test_commit_validation():
     assert call(args(B=0, lg=None)) == 0
 
 
+@pytest.mark.parametrize("kw,want", [
+    (dict(S=0), INVALID), (dict(B=-1), INVALID), (dict(Hkv=0), INVALID), (dict(D=0), INVALID),
+    (dict(Lmax=-1), INVALID), (dict(dtype=7), UNSUPPORTED), (dict(D=300), UNSUPPORTED),
+    (dict(S=2048), UNSUPPORTED), (dict(B=20000), UNSUPPORTED), (dict(B=4096, Lmax=65536), UNSUPPORTED),
+])
+def test_ctx_append_rejects_bad_shapes(kw, want):
+    L = tt.lib()
+    assert L.tt_ctx_append(ctypes.byref(_shape(**kw)), *([FAKE] * 5), 1, FAKE, None) == want
+
+
+def test_ctx_append_null_pointers_and_empty_batch():
+    L = tt.lib()
+    sh = _shape()
+    for k in range(5):
+        ptrs = [FAKE] * 5
+        ptrs[k] = None
+        assert L.tt_ctx_append(ctypes.byref(sh), *ptrs, 1, None, None) == INVALID
+    assert L.tt_ctx_append(None, *([FAKE] * 5), 1, None, None) == INVALID
+    assert L.tt_ctx_append(ctypes.byref(_shape(B=0)), *([None] * 5), 1, None, None) == 0
+
+
 def test_profile_api_without_gpu_work():
     tt.profile_enable(True)
     tt.profile_reset()

@@ -249,3 +249,69 @@ def test_commit_unmasked_rows_never_read(dev):
     got = _gpu_commit(d, dev, 0.4)
     for a, b in zip(base, got):
         assert np.array_equal(a, b)
+
+
+# ---- context cache update after a commit: bit-exact against the oracle -------------------------
+
+def _from_device(t, dtype):
+    if dtype == W.BF16:
+        return t.cpu().view(torch.int16).numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def _append_inputs(B, S, Hkv, D, Lmax, dtype, ctx, seed):
+    rng = np.random.default_rng(seed)
+    if dtype == W.BF16:
+        mk = lambda *sh: rng.integers(0, 1 << 16, size=sh, dtype=np.uint16)  # noqa: E731 (any bits, NaN included)
+    else:
+        mk = lambda *sh: rng.standard_normal(sh).astype(np.float32)  # noqa: E731
+    return mk(B, S, Hkv, D), mk(B, S, Hkv, D), mk(B, Lmax, Hkv, D), mk(B, Lmax, Hkv, D), \
+        np.array(ctx, dtype=np.int32)
+
+
+APPEND_CASES = [
+    # name, B, S, Hkv, D, Lmax, dtype, ctx_len, bump
+    ("bf16-edges", 7, 16, 2, 128, 64, W.BF16, [0, 1, 47, 48, 49, 64, -3], True),
+    ("bf16-no-bump", 3, 16, 2, 128, 40, W.BF16, [0, 10, 24], False),
+    ("f32-unaligned-rows", 4, 5, 3, 7, 30, W.F32, [0, 25, 26, 13], True),
+    ("bf16-unaligned-rows", 3, 3, 1, 5, 12, W.BF16, [9, 10, 2], True),
+    ("bf16-S1", 5, 1, 2, 64, 8, W.BF16, [0, 7, 8, 3, 6], True),
+    ("bf16-long-blocks", 2, 256, 4, 128, 1024, W.BF16, [700, 768], True),
+]
+
+
+@pytest.mark.parametrize("case", APPEND_CASES, ids=[c[0] for c in APPEND_CASES])
+def test_ctx_append_matches_oracle(dev, case):
+    import block_diffusion_lm_tt_amd as tt
+    from oracle import ttref_ctx_append
+    name, B, S, Hkv, D, Lmax, dtype, ctx, bump = case
+    _say(f"[ctx_append] {name}: B={B} S={S} Hkv={Hkv} D={D} Lmax={Lmax} {dtype} ctx={ctx} bump={bump}")
+    kn, vn, kc, vc, cl = _append_inputs(B, S, Hkv, D, Lmax, dtype, ctx, seed=B * 31 + S)
+    ek, ev, ecl, esk = ttref_ctx_append(B, S, Hkv, D, Lmax, dtype, kn, vn, kc, vc, cl, bump)
+    tkn, tvn = TZ.to_torch(kn, dtype, dev), TZ.to_torch(vn, dtype, dev)
+    tkc, tvc = TZ.to_torch(kc, dtype, dev), TZ.to_torch(vc, dtype, dev)
+    tcl = torch.from_numpy(cl).to(dev)
+    sk = tt.tt_ctx_append(tkn, tvn, tkc, tvc, tcl, bump=bump, want_skipped=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(sk.cpu().numpy(), esk)
+    assert np.array_equal(tcl.cpu().numpy(), ecl)
+    assert _from_device(tkc, dtype).tobytes() == ek.tobytes()
+    assert _from_device(tvc, dtype).tobytes() == ev.tobytes()
+
+
+def test_ctx_append_then_attention_matches_oracle(dev):
+    """The block loop's end: after the cache update (bump), attention over the grown context
+    agrees with the oracle on the same updated inputs."""
+    import block_diffusion_lm_tt_amd as tt
+    from oracle import ttref_ctx_append
+    x = W.make_attn(3, 16, 32, 2, 128, [100, 0, 300], Lmax=320, dtype=W.BF16, seed=11)
+    k2, v2, c2, _ = ttref_ctx_append(x.B, x.S, x.Hkv, x.D, x.Lmax, x.dtype, x.k_blk, x.v_blk, x.k_ctx,
+                                     x.v_ctx, x.ctx_len, True)
+    q, kb, vb, kc, vc, cl = TZ.attn_to_device(x, dev)
+    tt.tt_ctx_append(kb, vb, kc, vc, cl, bump=True)
+    out = tt.tt_block_denoise_attn(q, kb, vb, kc, vc, cl)
+    torch.cuda.synchronize()
+    y = W.AttnInputs(x.B, x.S, x.Hq, x.Hkv, x.D, x.Lmax, x.dtype, x.q, x.k_blk, x.v_blk, k2, v2, c2)
+    want = _oracle_attn(y)
+    err = float(np.abs(out.double().cpu().numpy() - want).max())
+    assert err <= TOL[W.BF16], err
