@@ -102,25 +102,34 @@ def loop_bench(w, args, torch, tt, TZ, W):
     tt_block_denoise_attn on every layer (its own context KV, block Q/K/V drawn per
     (step, layer)) and then tt_commit on that step's logits; the still-masked set shrinks
     by the committed positions, and the last step commits whatever is left (the end of a
-    block). Reported per gamma: blocks/s = B / (time of the T steps) and the positions
-    committed at each step. Inputs are generated and copied to HBM before timing."""
+    block) and every layer's context cache takes the block's rows (tt_ctx_append, the last
+    layer bumping ctx_len). Each block starts from the workload's context lengths again (the
+    caches have S spare rows past Lmax for the update). Reported per gamma: blocks/s = B /
+    (time of the T steps and the cache update) and the positions committed at each step.
+    Inputs are generated and copied to HBM before timing."""
     dev = torch.device("cuda:0")
     T, L = w.steps, w.layers
     log(f"[loop] generating workload {w.cid}: {w.name}")
-    ctx = torch.from_numpy(w.ctx_lens()).to(dev)
+    ctx0 = torch.from_numpy(w.ctx_lens()).to(dev)
+    ctx = ctx0.clone()
     kcs, vcs = [], []
     for l in range(L):
         x = w.attn(step=0, layer=l)
         _, _, _, kc, vc, _ = TZ.attn_to_device(x, dev)
-        kcs.append(kc)
-        vcs.append(vc)
-        del x
+        # S spare rows past Lmax: room for the committed block's rows
+        kb = torch.empty((w.B, w.Lmax + w.S, w.Hkv, w.D), dtype=kc.dtype, device=dev)
+        vb = torch.empty_like(kb)
+        kb[:, :w.Lmax].copy_(kc)
+        vb[:, :w.Lmax].copy_(vc)
+        kcs.append(kb)
+        vcs.append(vb)
+        del x, kc, vc
     qkv = [[tuple(TZ.to_torch(a, w.dtype, dev) for a in w.block_qkv(t, l)) for l in range(L)]
            for t in range(T)]
     logits = [TZ.commit_to_device(w.commit(step=t), dev)[0] for t in range(T)]
     out = torch.empty_like(qkv[0][0][0])
     dt = 1 if w.dtype == W.BF16 else 0
-    ws_a = torch.empty(max(1, tt.tt_block_denoise_attn_workspace(w.B, w.S, w.Hq, w.Hkv, w.D, w.Lmax, dt)),
+    ws_a = torch.empty(max(1, tt.tt_block_denoise_attn_workspace(w.B, w.S, w.Hq, w.Hkv, w.D, w.Lmax + w.S, dt)),
                        dtype=torch.uint8, device=dev)
     ws_c = torch.empty(max(1, tt.tt_commit_workspace(w.B, w.S, w.V, dt)), dtype=torch.uint8, device=dev)
     tok = torch.empty((w.B, w.S), dtype=torch.int32, device=dev)
@@ -131,6 +140,7 @@ def loop_bench(w, args, torch, tt, TZ, W):
 
     def block(gamma: float):
         mask.copy_(ones)
+        ctx.copy_(ctx0)
         for t in range(T):
             for l in range(L):
                 q, kb, vb = qkv[t][l]
@@ -141,6 +151,11 @@ def loop_bench(w, args, torch, tt, TZ, W):
                 com.copy_(mask)  # end of the block: every remaining masked position commits
             counts[t] += com.sum()
             mask.sub_(com)  # committed positions are masked ones: mask & ~committed
+        # the committed block's rows enter every layer's context cache (stand-in rows: the
+        # last step's block K/V of that layer); the last layer bumps ctx_len
+        for l in range(L):
+            _, kb, vb = qkv[T - 1][l]
+            tt.tt_ctx_append(kb, vb, kcs[l], vcs[l], ctx, bump=(l == L - 1))
 
     results = []
     reps = max(1, args.steps // 10)
@@ -163,6 +178,21 @@ def loop_bench(w, args, torch, tt, TZ, W):
                         "end_of_block_commits_per_sequence": per_step[-1]})
         log(f"[loop] gamma {gamma}: {ms:.3f} ms per block of {T} steps x {L} layers, "
             f"{w.B / (ms * 1e-3):.1f} blocks/s, committed per step per sequence {per_step}")
+    # the cache update alone: L layer calls, timed back-to-back
+    reps_a = 20
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps_a):
+        ctx.copy_(ctx0)
+        for l in range(L):
+            _, kb, vb = qkv[T - 1][l]
+            tt.tt_ctx_append(kb, vb, kcs[l], vcs[l], ctx, bump=(l == L - 1))
+    e1.record()
+    torch.cuda.synchronize()
+    append_us = e0.elapsed_time(e1) * 1e3 / (reps_a * L)
+    append_bytes = 2 * 2 * w.B * w.S * w.Hkv * w.D * (2 if w.dtype == W.BF16 else 4)  # read + write, K and V
+    log(f"[loop] context cache update: {append_us:.1f} us per layer ({append_bytes / append_us / 1e3:.1f} GB/s)")
     attn_flop = 4.0 * w.S * w.Hq * w.D * float((w.ctx_lens().astype(np.int64) + w.S).sum()) * L * T
     res = {"metric": "block-loop blocks/s and tokens committed per step", "unit": "blocks/s",
            "value": results[1]["blocks_per_s"], "n_gpus": 1, "higher_is_better": True,
@@ -171,6 +201,8 @@ def loop_bench(w, args, torch, tt, TZ, W):
                       "ctx_len": int(w.ctx_lens()[0]), "layers": L, "steps": T, "V": w.V,
                       "reps": reps},
            "attn_mfma_TFLOPs_gamma_0.8": attn_flop / (results[1]["ms_per_block"] * 1e-3) / 1e12,
+           "ctx_append_us_per_layer": append_us,
+           "ctx_append_GBps": append_bytes / append_us / 1e3,
            "sweep": results}
     print(json.dumps(res), flush=True)
 
