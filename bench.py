@@ -16,6 +16,7 @@ context-KV stream's achieved HBM bandwidth against the 8 TB/s peak.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import math
 import os
@@ -214,6 +215,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=3, help="workload id; the headline line is 3")
     ap.add_argument("--rotate", type=int, default=4, help="copies of context KV / logits cycled")
+    ap.add_argument("--block-size", type=int, default=0,
+                    help="block positions S of the workload (0: its own; other sizes are extra lines, "
+                         "not the headline)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work sampled")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -240,6 +244,8 @@ def main():
     dev = torch.device("cuda:0")
     tt.lib()
     w = W.WORKLOADS[args.config]
+    if args.block_size:
+        w = dataclasses.replace(w, S=args.block_size, name=f"{w.name} (block size S={args.block_size})")
     if w.layers != 1:
         loop_bench(w, args, torch, tt, TZ, W)
         return
@@ -353,7 +359,8 @@ def main():
         "mfma_pct_bf16_peak": 100.0 * tflops / MFMA_BF16_PEAK_TFLOPS,
         "roofline": {"kernel": "attn_mfma_kernel", "bound": "hbm", "achieved": gbs_main,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs_main / HBM_PEAK_GBS,
-                     "traffic": profiled_traffic("attn_mfma_kernel") if args.config == 3 else None,
+                     "traffic": profiled_traffic("attn_mfma_kernel")
+                     if args.config == 3 and not args.block_size else None,
                      "avg_us": t_main * 1e6, "algorithmic_bytes_per_launch": kv_bytes},
         "cpu_baseline": cpu,
     }

@@ -75,6 +75,8 @@ ATTN_CASES = [
     ("mfma-tiny-rows", 2, 5, 6, 2, 128, [64, 129], 200, W.BF16),
     ("mfma-S1", 4, 1, 16, 1, 128, [1, 63, 64, 65], 70, W.BF16),
     ("mfma-S64-NQ8", 2, 64, 32, 2, 128, [500, 31], 512, W.BF16),
+    ("mfma-S32-NQ2", 3, 32, 32, 2, 128, [700, 33, 260], 704, W.BF16),
+    ("mfma-S128-NQ8", 1, 128, 32, 2, 128, [900], 900, W.BF16),
     ("mfma-ctx0", 2, 16, 32, 2, 128, [0, 0], 0, W.BF16),
     ("mfma-G1", 2, 16, 4, 4, 128, [130, 7], 130, W.BF16),
     ("mfma-long-split", 1, 16, 32, 2, 128, [9000], 9000, W.BF16),
