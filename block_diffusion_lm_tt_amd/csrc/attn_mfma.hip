@@ -12,7 +12,8 @@
 //    with v_mfma_f32_32x32x16_bf16. A workgroup of 8 waves covers 256 query rows, 32 per
 //    wave; one workgroup per CU, two waves per SIMD. A unit with more rows is covered by
 //    NQ workgroups (a "cluster") placed on one XCD so that its key stream is fetched from
-//    HBM once and shared through that XCD's L2.
+//    HBM once and shared through that XCD's L2. Clusters are numbered XCD-major: the
+//    clusters that hold the pieces of one cut unit sit on one XCD and share its query rows.
 //  * Keys of a unit are the concatenation [context ; block]; the key sequence is cut in
 //    32-key tiles. All units form one global list of positions, each unit a fixed number
 //    of overhead positions (the cost of a segment, in tiles) followed by its tiles; the
@@ -451,7 +452,9 @@ __global__ __launch_bounds__(NTHR, 1) void attn_mfma_kernel(AttnArgs a) {
   const int lr = lane & 31, lh = lane >> 5;
   const int id = bid_x();
   const int xcd = id & 7, kk = id >> 3;
-  const int cluster = __builtin_amdgcn_readfirstlane((kk / a.NQ) * 8 + xcd);
+  // workgroup id % 8 is its XCD; clusters are numbered XCD-major, so the consecutive
+  // clusters that share a cut unit also share an L2 and fetch its query rows once
+  const int cluster = __builtin_amdgcn_readfirstlane(xcd * (a.NC / 8) + kk / a.NQ);
   const int qs = __builtin_amdgcn_readfirstlane(kk % a.NQ);
 
   // ---- plan: position prefix sums in LDS, then this cluster's range of the global list
