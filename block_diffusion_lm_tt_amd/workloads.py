@@ -34,7 +34,7 @@ F32 = "f32"
 BF16 = "bf16"
 
 # tensor ids for the per-tensor random streams
-_T_Q, _T_KB, _T_VB, _T_KC, _T_VC, _T_LEN, _T_LOGIT, _T_MASK, _T_PEAK, _T_BIAS = range(10)
+_T_Q, _T_KB, _T_VB, _T_KC, _T_VC, _T_LEN, _T_LOGIT, _T_MASK, _T_PEAK, _T_BIAS, _T_HID, _T_HEAD = range(12)
 
 BF16_NAN = np.uint16(0x7FC0)
 
@@ -107,6 +107,51 @@ class CommitInputs:
     def masked_row_bytes(self) -> int:
         elt = 4 if self.dtype == F32 else 2
         return int(self.mask.astype(np.int64).sum()) * self.V * elt
+
+
+@dataclasses.dataclass
+class LmHeadInputs:
+    B: int
+    S: int
+    K: int          # d_model
+    V: int
+    hidden: np.ndarray  # uint16 (bf16 bits) [B,S,K]
+    weight: np.ndarray  # uint16 (bf16 bits) [V,K], one row per vocabulary entry
+    mask: np.ndarray    # uint8 [B,S]
+    gamma: float
+
+
+def make_lmhead(B: int, S: int, K: int, V: int, seed: int = 0, step: int = 0, gamma: float = 0.8,
+                mask: Optional[np.ndarray] = None, sigma: float = 3.0,
+                peaks: Optional[dict] = None) -> LmHeadInputs:
+    """Hidden states N(0, 1) [B,S,K] and LM-head weights N(0, sigma/sqrt(K)) [V,K], both
+    rounded to bf16, so that a logit has standard deviation about sigma.
+
+    ``peaks``: ``{"p": 0.6, "low": 8.0, "high": 14.0}`` picks, independently per position
+    with probability p, a random token v and a height h ~ U(low, high), and adds
+    (h / |w_v|^2) * w_v to the position's hidden state (before rounding): that token's
+    logit rises by about h.
+    """
+    wsc = float(sigma) / math.sqrt(K)
+    rw = _rng(seed, _T_HEAD)
+    w32 = np.empty((V, K), dtype=np.float32)
+    for v0 in range(0, V, 8192):  # chunked draws keep the fp32 staging small
+        w32[v0:v0 + 8192] = _normal(rw, (min(8192, V - v0), K), wsc)
+    w = f32_to_bf16_bits(w32)
+    del w32
+    h = _normal(_rng(seed, _T_HID, step), (B, S, K))
+    if peaks:
+        rp = _rng(seed, _T_PEAK, step)
+        hit = rp.random((B, S)) < float(peaks.get("p", 0.6))
+        ids = rp.integers(0, V, size=(B, S))
+        ht = rp.uniform(float(peaks.get("low", 8.0)), float(peaks.get("high", 14.0)), size=(B, S))
+        for b, i in zip(*np.nonzero(hit)):
+            wv = bf16_bits_to_f32(w[ids[b, i]]).astype(np.float64)
+            h[b, i] += (ht[b, i] / float(wv @ wv) * wv).astype(np.float32)
+    if mask is None:
+        mask = np.ones((B, S), dtype=np.uint8)
+    return LmHeadInputs(B, S, K, V, f32_to_bf16_bits(h), w, np.ascontiguousarray(mask, dtype=np.uint8),
+                        float(np.float32(gamma)))
 
 
 def make_attn(B: int, S: int, Hq: int, Hkv: int, D: int, ctx_lens: Sequence[int] | np.ndarray,

@@ -40,6 +40,7 @@
 
 #define TTREF_F32 0
 #define TTREF_BF16 1
+#define TTREF_F64 2 /* internal: logits the oracle computed itself */
 
 #define TTREF_OK 0
 #define TTREF_EINVAL 1
@@ -50,6 +51,8 @@ static double ttref_load(const void *base, size_t idx, int dtype)
 {
     if (dtype == TTREF_F32)
         return (double)((const float *)base)[idx];
+    if (dtype == TTREF_F64)
+        return ((const double *)base)[idx];
     uint32_t bits = ((uint32_t)((const uint16_t *)base)[idx]) << 16;
     float f;
     memcpy(&f, &bits, sizeof f);
@@ -185,15 +188,10 @@ int ttref_block_denoise_attn(int B, int S, int Hq, int Hkv, int D, int Lmax, int
  * Unmasked positions: token = -1, committed = 0, conf = 0, Z = 0. Their rows are not read.
  * Outputs token_id[B,S] int32, committed[B,S] uint8; conf and Z ([B,S] double) may be NULL.
  */
-int ttref_commit(int B, int S, int V, int dtype, const void *logits, const uint8_t *mask,
-                 double gamma, int32_t *token_id, uint8_t *committed, double *conf_out,
-                 double *z_out)
+static void ttref_commit_rows(int B, int S, int V, int dtype, const void *logits,
+                              const uint8_t *mask, double gamma, int32_t *token_id,
+                              uint8_t *committed, double *conf_out, double *z_out)
 {
-    if (B < 0 || S < 1 || V < 1 || isnan(gamma))
-        return TTREF_EINVAL;
-    if (dtype != TTREF_F32 && dtype != TTREF_BF16)
-        return TTREF_EINVAL;
-
 #pragma omp parallel for schedule(dynamic)
     for (int b = 0; b < B; ++b) {
         int any_masked = 0, any_committed = 0;
@@ -240,6 +238,62 @@ int ttref_commit(int B, int S, int V, int dtype, const void *logits, const uint8
         if (any_masked && !any_committed)
             committed[(size_t)b * S + best_i] = 1;
     }
+}
+
+int ttref_commit(int B, int S, int V, int dtype, const void *logits, const uint8_t *mask,
+                 double gamma, int32_t *token_id, uint8_t *committed, double *conf_out,
+                 double *z_out)
+{
+    if (B < 0 || S < 1 || V < 1 || isnan(gamma))
+        return TTREF_EINVAL;
+    if (dtype != TTREF_F32 && dtype != TTREF_BF16)
+        return TTREF_EINVAL;
+    ttref_commit_rows(B, S, V, dtype, logits, mask, gamma, token_id, committed, conf_out, z_out);
+    return TTREF_OK;
+}
+
+/*
+ * The LM head followed by confidence unmasking ([GS] Training and Conditioning > Sampling:
+ * all masked tokens are predicted at once from the denoiser's output; [SN] Blockwise
+ * generering i praksis). The step's logits are the LM head's output for the hidden state
+ * h[b,i,0:K] of every still-masked position (K = d_model) and the head's weight rows
+ * w[v,0:K] (vocabulary-major, as the head's [V, K] matrix):
+ *   l[b,i,v] = sum_k h[b,i,k] * w[v,k]
+ * Each product of two bf16 values is exact in double and the sum runs over k in ascending
+ * order in double. The commit rule of ttref_commit is then applied to these logits.
+ * Hidden rows of unmasked positions are not read. Inputs are bf16 bit patterns.
+ */
+int ttref_lmhead_commit(int B, int S, int K, int V, const uint16_t *hidden,
+                        const uint16_t *weight, const uint8_t *mask, double gamma,
+                        int32_t *token_id, uint8_t *committed, double *conf_out, double *z_out)
+{
+    if (B < 0 || S < 1 || K < 1 || V < 1 || isnan(gamma))
+        return TTREF_EINVAL;
+    double *lg = (double *)malloc((size_t)S * V * sizeof(double));
+    if (!lg)
+        return TTREF_ENOMEM;
+    for (int b = 0; b < B; ++b) {
+        for (int i = 0; i < S; ++i) {
+            const size_t r = (size_t)b * S + i;
+            if (!mask[r])
+                continue;
+            const size_t hoff = r * (size_t)K;
+#pragma omp parallel for schedule(static)
+            for (int v = 0; v < V; ++v) {
+                const size_t woff = (size_t)v * K;
+                double dot = 0.0;
+                for (int k = 0; k < K; ++k)
+                    dot += ttref_load(hidden, hoff + k, TTREF_BF16) *
+                           ttref_load(weight, woff + k, TTREF_BF16);
+                lg[(size_t)i * V + v] = dot;
+            }
+        }
+        ttref_commit_rows(1, S, V, TTREF_F64, lg, mask + (size_t)b * S, gamma,
+                          token_id + (size_t)b * S, committed + (size_t)b * S,
+                          conf_out ? conf_out + (size_t)b * S : NULL,
+                          z_out ? z_out + (size_t)b * S : NULL);
+    }
+    free(lg);
     return TTREF_OK;
 }
 

@@ -35,6 +35,8 @@ def _lib():
         L.ttref_commit.restype = i32
         L.ttref_decode.argtypes = [vp, ctypes.c_size_t, i32]
         L.ttref_decode.restype = ctypes.c_double
+        L.ttref_lmhead_commit.argtypes = [i32] * 4 + [vp] * 3 + [ctypes.c_double] + [vp] * 4
+        L.ttref_lmhead_commit.restype = i32
         L.ttref_ctx_append.argtypes = [i32] * 6 + [vp] * 5 + [i32, vp]
         L.ttref_ctx_append.restype = i32
         L.ttref_threads.argtypes = []
@@ -96,6 +98,25 @@ def ttref_commit(B, S, V, dtype, logits, mask, gamma):
                              _ptr(com), _ptr(conf), _ptr(z))
     if rc != 0:
         raise ValueError(f"ttref_commit failed with status {rc}")
+    return tok, com, conf, z
+
+
+def ttref_lmhead_commit(B, S, K, V, hidden, weight, mask, gamma):
+    """LM head then commit: hidden uint16 (bf16 bits) [B,S,K], weight uint16 [V,K].
+    Returns (token_id int32[B,S], committed uint8[B,S], conf f64[B,S], Z f64[B,S])."""
+    _check_dtype(hidden, "bf16")
+    _check_dtype(weight, "bf16")
+    assert hidden.size == B * S * K and weight.size == V * K
+    m = np.ascontiguousarray(mask, dtype=np.uint8)
+    assert m.size == B * S
+    tok = np.zeros((B, S), dtype=np.int32)
+    com = np.zeros((B, S), dtype=np.uint8)
+    conf = np.zeros((B, S), dtype=np.float64)
+    z = np.zeros((B, S), dtype=np.float64)
+    rc = _lib().ttref_lmhead_commit(B, S, K, V, _ptr(hidden), _ptr(weight), _ptr(m), float(gamma),
+                                    _ptr(tok), _ptr(com), _ptr(conf), _ptr(z))
+    if rc != 0:
+        raise ValueError(f"ttref_lmhead_commit failed with status {rc}")
     return tok, com, conf, z
 
 

@@ -3,7 +3,8 @@
 Each case copies oracle/ttref.c, applies one plausible slip (a dropped scale, a flipped
 sign, a wrong KV-head index, a transposed layout, values read from K, a dropped block key,
 >= instead of >, a wrong tie rule, a missing fallback, a cache update at the wrong rows,
-without the length bump or with an off-by-one fit test), builds that copy into a temporary
+without the length bump or with an off-by-one fit test, an LM head read transposed, from
+the wrong sequence, short of its last feature or with a flipped product), builds that copy into a temporary
 library and runs the pin suite against it in a child process. The suite must fail.
 """
 import os
@@ -29,6 +30,14 @@ MUTANTS = {
     "no_fallback": ("if (any_masked && !any_committed)", "if (0)"),
     "z_sign": ("z += exp(ttref_load(logits, off + v, dtype) - m);",
                "z += exp(m - ttref_load(logits, off + v, dtype));"),
+    "lmhead_weight_transposed": ("ttref_load(weight, woff + k, TTREF_BF16);",
+                                 "ttref_load(weight, (size_t)k * V + v, TTREF_BF16);"),
+    "lmhead_hidden_ignores_sequence": ("const size_t hoff = r * (size_t)K;",
+                                       "const size_t hoff = (size_t)i * K;"),
+    "lmhead_drops_last_feature": ("for (int k = 0; k < K; ++k)\n                    dot +=",
+                                  "for (int k = 0; k < K - 1; ++k)\n                    dot +="),
+    "lmhead_product_sign": ("dot += ttref_load(hidden, hoff + k, TTREF_BF16) *",
+                            "dot -= ttref_load(hidden, hoff + k, TTREF_BF16) *"),
     "append_ignores_length": ("const size_t dst = ((size_t)b * Lmax + n + i) * row;",
                               "const size_t dst = ((size_t)b * Lmax + i) * row;"),
     "append_no_bump": ("ctx_len[b] = n + S;", "ctx_len[b] = n;"),

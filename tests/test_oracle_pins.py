@@ -15,7 +15,7 @@ import scipy.special
 import torch
 
 from block_diffusion_lm_tt_amd import workloads as W
-from oracle import ttref_block_denoise_attn, ttref_commit, ttref_ctx_append, ttref_decode
+from oracle import ttref_block_denoise_attn, ttref_commit, ttref_ctx_append, ttref_decode, ttref_lmhead_commit
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -324,6 +324,84 @@ def test_commit_rejects_nan_gamma():
     with pytest.raises(ValueError):
         _commit(c, float("nan"))
 
+
+
+# ---- LM head followed by the commit ------------------------------------------------------------
+
+def _lmhead(x: W.LmHeadInputs, gamma=None):
+    return ttref_lmhead_commit(x.B, x.S, x.K, x.V, x.hidden, x.weight, x.mask,
+                               x.gamma if gamma is None else gamma)
+
+
+def _int_bf16(rng, shape, lo, hi):
+    """Small integers as bf16 bits (exact), so that every logit is an exact integer."""
+    return W.f32_to_bf16_bits(rng.integers(lo, hi + 1, size=shape).astype(np.float32))
+
+
+@pytest.mark.parametrize("gamma", [0.0, 0.3, 0.8, 1.5])
+def test_lmhead_on_integer_data_equals_commit_of_the_exact_logits(gamma):
+    # integer hidden states and weights: numpy's int64 product gives the logits exactly, and
+    # the commit of those logits (an fp32 tensor holding them exactly) must agree bit for bit
+    rng = np.random.default_rng(11)
+    B, S, K, V = 3, 8, 48, 300
+    h = _int_bf16(rng, (B, S, K), -3, 3)
+    w = _int_bf16(rng, (V, K), -2, 2)
+    mask = W.random_mask(B, S, 0, S, seed=4)
+    hi = W.bf16_bits_to_f32(h).astype(np.int64)
+    wi = W.bf16_bits_to_f32(w).astype(np.int64)
+    logits = np.einsum("bsk,vk->bsv", hi, wi).astype(np.float32)  # |l| <= 288: exact
+    ref = ttref_commit(B, S, V, "f32", np.ascontiguousarray(logits), mask, gamma)
+    got = ttref_lmhead_commit(B, S, K, V, h, w, mask, gamma)
+    for r, g in zip(ref, got):
+        assert np.array_equal(r, g)
+    assert (logits.max(-1, keepdims=True) == logits).sum(-1).max() > 1  # the tie rule is exercised
+
+
+def test_lmhead_matches_library_fp64_matmul_argmax_and_softmax():
+    x = W.make_lmhead(2, 8, 192, 1000, seed=9, gamma=0.6, mask=W.random_mask(2, 8, 3, 8, seed=2),
+                      peaks={"p": 0.5, "low": 4.0, "high": 9.0})
+    tok, com, conf, z = _lmhead(x)
+    h = _dec(x.hidden, W.BF16).numpy()
+    w = _dec(x.weight, W.BF16).numpy()
+    logits = h @ w.T  # numpy fp64 matmul of the library-decoded inputs
+    for b in range(x.B):
+        masked = [i for i in range(x.S) if x.mask[b, i]]
+        for i in range(x.S):
+            if not x.mask[b, i]:
+                assert tok[b, i] == -1 and com[b, i] == 0 and conf[b, i] == 0
+                continue
+            row = logits[b, i]
+            assert tok[b, i] == np.argmax(row)
+            np.testing.assert_allclose(conf[b, i], scipy.special.softmax(row).max(), rtol=1e-12)
+            np.testing.assert_allclose(z[b, i], math.exp(scipy.special.logsumexp(row) - row.max()), rtol=1e-12)
+        above = [i for i in masked if conf[b, i] > x.gamma]
+        want = above if above else ([max(masked, key=lambda i: conf[b, i])] if masked else [])
+        assert sorted(np.nonzero(com[b])[0].tolist()) == sorted(want)
+
+
+def test_lmhead_closed_form_one_hot_head():
+    # head rows w_v = 2 e_v (V = K), hidden state c e_j: logits 2c at j, 0 elsewhere
+    K = V = 64
+    w = W.f32_to_bf16_bits(2.0 * np.eye(V, K, dtype=np.float32))
+    hid = np.zeros((1, 3, K), np.float32)
+    hid[0, 0, 5], hid[0, 1, 40], hid[0, 2, 63] = 1.0, 3.0, 0.5
+    tok, com, conf, z = ttref_lmhead_commit(1, 3, K, V, W.f32_to_bf16_bits(hid), w,
+                                            np.ones((1, 3), np.uint8), 0.5)
+    assert tok.tolist() == [[5, 40, 63]]
+    for i, c in enumerate([1.0, 3.0, 0.5]):
+        assert conf[0, i] == pytest.approx(1.0 / (1.0 + (V - 1) * math.exp(-2.0 * c)), rel=1e-14)
+    assert com.tolist() == [[0, 1, 0]]  # only 2c = 6 clears 0.5
+
+
+def test_lmhead_does_not_read_unmasked_hidden_rows():
+    x = W.make_lmhead(2, 6, 32, 200, seed=3, mask=np.array([[1, 0, 1, 0, 0, 1], [0, 0, 0, 0, 0, 0]], np.uint8))
+    ref = _lmhead(x)
+    hid = x.hidden.copy()
+    hid[x.mask == 0] = W.BF16_NAN
+    got = ttref_lmhead_commit(x.B, x.S, x.K, x.V, hid, x.weight, x.mask, x.gamma)
+    for r, g in zip(ref, got):
+        assert np.array_equal(r, g)
+    assert got[1][1].sum() == 0 and np.all(got[0][1] == -1)
 
 
 # ---- context cache update after a commit ------------------------------------------------------
