@@ -37,7 +37,9 @@ class AttnShape(ctypes.Structure):
 class ProfileStats(ctypes.Structure):
     _fields_ = [("attn_calls", ctypes.c_int64), ("attn_total_ms", ctypes.c_double),
                 ("attn_main_ms", ctypes.c_double), ("commit_calls", ctypes.c_int64),
-                ("commit_total_ms", ctypes.c_double), ("commit_reduce_ms", ctypes.c_double)]
+                ("commit_total_ms", ctypes.c_double), ("commit_reduce_ms", ctypes.c_double),
+                ("lm_calls", ctypes.c_int64), ("lm_total_ms", ctypes.c_double),
+                ("lm_reduce_ms", ctypes.c_double)]
 
 
 _LIB = None
@@ -66,6 +68,10 @@ def lib() -> ctypes.CDLL:
         L.tt_commit_workspace.argtypes = [i32, i32, i32, i32]
         L.tt_commit.restype = i32
         L.tt_commit.argtypes = [i32, i32, i32, i32, vp, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp]
+        L.tt_lmhead_commit_workspace.restype = sz
+        L.tt_lmhead_commit_workspace.argtypes = [i32, i32, i32, i32]
+        L.tt_lmhead_commit.restype = i32
+        L.tt_lmhead_commit.argtypes = [i32, i32, i32, i32, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp]
         L.tt_profile_enable.restype = i32
         L.tt_profile_enable.argtypes = [i32]
         L.tt_profile_reset.restype = i32
@@ -201,6 +207,55 @@ def tt_commit(logits, mask, gamma: float, token_id=None, committed=None, conf=No
                          committed.data_ptr(), conf.data_ptr() if conf is not None else None,
                          workspace.data_ptr(), workspace.numel(), _stream(dev, stream))
     _check("tt_commit", st)
+    return token_id, committed, conf
+
+
+def tt_lmhead_commit_workspace(B, S, K, V) -> int:
+    return int(lib().tt_lmhead_commit_workspace(B, S, K, V))
+
+
+def tt_lmhead_commit(hidden, weight, mask, gamma: float, token_id=None, committed=None, conf=None,
+                     want_conf: bool = True, workspace=None, stream=None):
+    """LM head + commit (see include/tt.h): hidden bf16 [B,S,K], weight bf16 [V,K], mask uint8
+    [B,S]. Returns (token_id int32[B,S], committed uint8[B,S], conf float32[B,S] or None)."""
+    torch = _torch()
+    _dev(hidden, "hidden")
+    _dev(weight, "weight")
+    _dev(mask, "mask")
+    if hidden.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
+        raise TypeError("hidden and weight must be bfloat16")
+    if hidden.dim() != 3 or weight.dim() != 2 or weight.shape[1] != hidden.shape[2]:
+        raise ValueError("hidden must be [B,S,K] and weight [V,K]")
+    B, S, K = hidden.shape
+    V = weight.shape[0]
+    if mask.dtype != torch.uint8 or mask.shape != (B, S):
+        raise ValueError("mask must be uint8 [B,S]")
+    dev = hidden.device
+    if token_id is None:
+        token_id = torch.empty((B, S), dtype=torch.int32, device=dev)
+    if committed is None:
+        committed = torch.empty((B, S), dtype=torch.uint8, device=dev)
+    if conf is None and want_conf:
+        conf = torch.empty((B, S), dtype=torch.float32, device=dev)
+    if token_id.dtype != torch.int32 or token_id.shape != (B, S):
+        raise ValueError("token_id must be int32 [B,S]")
+    if committed.dtype != torch.uint8 or committed.shape != (B, S):
+        raise ValueError("committed must be uint8 [B,S]")
+    _dev(token_id, "token_id")
+    _dev(committed, "committed")
+    if conf is not None:
+        if conf.dtype != torch.float32 or conf.shape != (B, S):
+            raise ValueError("conf must be float32 [B,S]")
+        _dev(conf, "conf")
+    need = tt_lmhead_commit_workspace(B, S, K, V)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _dev(workspace, "workspace")
+    st = lib().tt_lmhead_commit(B, S, K, V, hidden.data_ptr(), weight.data_ptr(), mask.data_ptr(),
+                                float(gamma), token_id.data_ptr(), committed.data_ptr(),
+                                conf.data_ptr() if conf is not None else None, workspace.data_ptr(),
+                                workspace.numel(), _stream(dev, stream))
+    _check("tt_lmhead_commit", st)
     return token_id, committed, conf
 
 

@@ -23,7 +23,8 @@
 //     more than 4e-4. Positions inside a band are recomputed by the same workgroup over the
 //     full row with fp64 exp and decided on those values (conf = 1/Z > gamma, in fp64 as in
 //     exact arithmetic), so every integer output is the exact-arithmetic decision except
-//     for margins below fp64 rounding.
+//     for margins below fp64 rounding. Called behind the fused LM head (no logits in
+//     memory), the same kernel decides on the chunk estimates alone, without the bands.
 #include "tt_internal.h"
 
 namespace tt {
@@ -210,6 +211,7 @@ __global__ __launch_bounds__(DT) void commit_decide_kernel(CommitArgs a) {
   double zz[MAXP];
   int tk[MAXP], fl[MAXP], dec[MAXP];
   int any_c = 0, nflag = 0, nmask = 0;
+  const bool exact = a.logits != nullptr;  // else: no logits to recompute from
 #pragma unroll
   for (int p = 0; p < MAXP; ++p) {
     const int i = tid + p * DT;
@@ -239,7 +241,7 @@ __global__ __launch_bounds__(DT) void commit_decide_kernel(CommitArgs a) {
     tk[p] = tok;
     zz[p] = Z;
     const double zg = Z * (double)a.gamma;
-    if (fabs(zg - 1.0) <= kBand) {
+    if (exact && fabs(zg - 1.0) <= kBand) {
       fl[p] = 1;
       ++nflag;
     } else {
@@ -268,7 +270,7 @@ __global__ __launch_bounds__(DT) void commit_decide_kernel(CommitArgs a) {
     for (int p = 0; p < MAXP; ++p)
       if (msk[p] && tid + p * DT != bi) my2 = fmax(my2, 1.0 / zz[p]);
     const double second = dblock_max(my2, redd);
-    if (nflag_tot > 0 || (second >= 0.0 && best <= second * (1.0 + kFallBand))) {
+    if (exact && (nflag_tot > 0 || (second >= 0.0 && best <= second * (1.0 + kFallBand)))) {
       fallback_pending = true;
 #pragma unroll
       for (int p = 0; p < MAXP; ++p)
@@ -340,6 +342,11 @@ __global__ __launch_bounds__(DT) void commit_decide_kernel(CommitArgs a) {
 }
 
 }  // namespace
+
+hipError_t launch_commit_decide(const CommitArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(commit_decide_kernel<uint16_t>, dim3(a.B), dim3(DT), 0, s, a);
+  return hipGetLastError();
+}
 
 int commit_chunk_elems(int dtype) { return NT * LOADS * (dtype == TT_BF16 ? 8 : 4); }
 

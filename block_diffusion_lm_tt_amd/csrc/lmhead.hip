@@ -1,0 +1,300 @@
+// LM head fused with the commit's vocabulary reduction, bf16, on gfx950 MFMA.
+//
+// What it computes: Nemotron-TwoTower (gist.science explainer), Technical Summary > Training
+// and Conditioning > Sampling -- every still-masked position of the block is predicted at
+// once from the denoiser's output, and confidence decides which are committed (the snilld.dk
+// TwoTower article, "Blockwise generering i praksis"). Here the prediction's last step, the
+// LM head, is computed and reduced in one pass: for every masked position (b,i) with hidden
+// state h[b,i,0:K] and every vocabulary entry v with head row w[v,0:K],
+//   l[b,i,v] = sum_k h[b,i,k] * w[v,k]      (bf16 inputs, fp32 accumulation)
+// and, per 256-entry vocabulary chunk, the chunk max, the lowest index attaining it and
+// sum_v exp(l_v - chunk max). The logits never reach memory. The commit's decide step then
+// merges the chunks of each row (token, Z, conf = 1/Z) and applies the gamma rule.
+//
+// How (MI355X design):
+//  * One workgroup = 256 head rows (a vocabulary tile) x 128 masked hidden rows (a row
+//    group), 8 waves of 64 x 64, each wave a 2 x 2 block of v_mfma_f32_32x32x16_bf16 with
+//    the head rows on the M side and the hidden rows on the N side (C^T = W H^T): both
+//    operands are 16-byte row-major reads of K-contiguous rows. fp32 accumulators stay in
+//    registers for the whole K loop.
+//  * K runs in stages of 64 features. A stage (32 KB of head rows + 16 KB of hidden rows)
+//    goes HBM -> LDS directly (global_load_lds_dwordx4, six 1-KB copies per wave) into a
+//    ring of 3 stages: two in flight while one is read; one barrier per stage. Each
+//    128-byte LDS row holds its eight 16-byte chunks permuted by slot = chunk ^ ((row/2)%8)
+//    (applied on the global side of the copy), so the 16 lanes of one ds_read_b128 pass
+//    (16 consecutive rows, one chunk) hit 16 distinct bank groups.
+//  * The masked rows are compacted inside the kernel (a ballot scan of the mask by every
+//    workgroup), so the launch needs no host synchronisation; a row group past the number
+//    of masked rows exits at once, and the last group pads with its first row (results
+//    discarded).
+//  * The row groups of one vocabulary tile are consecutive workgroups of one XCD (workgroup
+//    id % 8 is its XCD), so they run together and the tile's head rows come from HBM once
+//    and from that XCD's L2 for the others.
+//  * Epilogue: each lane holds 32 logits of one row; a lane scans them in increasing
+//    vocabulary order (max, lowest argmax), sums exp relative to its max, merges with the
+//    lane holding the row's other 32 (lanes l, l^32), and the four waves of a row merge
+//    through LDS in vocabulary order into the chunk record (z widened to fp64).
+#include "tt_internal.h"
+
+namespace tt {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int VT = kLmVocabPerWg;     // 256 head rows per workgroup
+constexpr int RT = kLmRowsPerWg;      // 128 hidden rows per workgroup
+constexpr int KS = kLmFeaturesPerStage;  // 64 features per stage
+constexpr int ROWB = KS * 2;          // 128-byte LDS rows
+constexpr int WTB = VT * ROWB;        // 32 KB of head rows per stage
+constexpr int HTB = RT * ROWB;        // 16 KB of hidden rows per stage
+constexpr int STB = WTB + HTB;        // 48 KB per stage
+constexpr int NSTG = 3;
+constexpr int NW = 8;
+constexpr int NTHR = NW * 64;
+constexpr int WDMA = WTB / 1024 / NW;  // 4 copies of head rows per wave per stage
+constexpr int HDMA = HTB / 1024 / NW;  // 2 copies of hidden rows per wave per stage
+constexpr int DMA_PER_STAGE = WDMA + HDMA;
+constexpr float kLog2e = 1.4426950408889634f;
+
+static_assert(RT == 2 * 64 && VT == 4 * 64, "waves: 2 row blocks x 4 vocabulary blocks of 64");
+static_assert(ROWB * 8 == 1024, "one copy = 8 LDS rows");
+static_assert(NSTG * STB <= 160 * 1024 - 8 * 1024, "ring and epilogue fit the LDS");
+
+__shared__ __attribute__((aligned(1024))) char g_lds[NSTG * STB];
+__shared__ int g_rows[RT];
+__shared__ int g_wcnt[NW];
+
+// wait until at most n vector-memory operations of this wave are outstanding (n <= 63)
+#define LM_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x70 | 0xF00)
+
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const char*>((uintptr_t)((hi << 32) | lo));
+}
+
+// One global -> LDS copy of 16 bytes per lane from a wave-uniform base plus a 32-bit lane
+// offset; lane i's bytes land at LDS byte lds + 16 i. As asm so that the compiler does not
+// make later LDS reads wait for it; completion is awaited explicitly (vmcnt) before the
+// barrier that publishes a stage. No register result.
+__device__ __forceinline__ void dma16u(const char* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:0" ::"v"(voff),
+               "s"(base), "s"(lds)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
+}
+
+// (m, tok, z) merge of two partials over disjoint vocabulary sets: larger max wins, equal
+// maxima keep the lower index; z moves to the common max. An empty partial has m = -inf.
+__device__ __forceinline__ void part_merge(float& m, int& tok, float& z, float m2, int tok2, float z2) {
+  if (m2 == -INFINITY) return;
+  if (m == -INFINITY) {
+    m = m2;
+    tok = tok2;
+    z = z2;
+    return;
+  }
+  const float M = fmaxf(m, m2);
+  z = z * exp2f((m - M) * kLog2e) + z2 * exp2f((m2 - M) * kLog2e);
+  if (m2 > m || (m2 == m && tok2 < tok)) tok = tok2;
+  m = M;
+}
+
+__global__ __launch_bounds__(NTHR, 1) void lmhead_reduce_kernel(LmHeadArgs a) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int id = blockIdx.x;
+  const int xcd = id & 7, kk = id >> 3;
+  const int rg = __builtin_amdgcn_readfirstlane(kk % a.NRG);
+  const int vt = __builtin_amdgcn_readfirstlane((kk / a.NRG) * 8 + xcd);
+  if (vt >= a.NVT) return;
+
+  // ---- this row group's masked rows (ballot scan of the mask, in position order)
+  const int BS = a.B * a.S;
+  int total = 0;
+  for (int p0 = 0; p0 < BS; p0 += NTHR) {
+    const int p = p0 + tid;
+    const bool m = p < BS && a.mask[p] != 0;
+    const uint64_t bal = __ballot(m);
+    const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+    if (lane == 0) g_wcnt[wave] = __popcll(bal);
+    __syncthreads();
+    int before = total, chunk = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const int c = g_wcnt[w];
+      before += w < wave ? c : 0;
+      chunk += c;
+    }
+    const int idx = before + below - rg * RT;
+    if (m && idx >= 0 && idx < RT) g_rows[idx] = p;
+    total += chunk;
+    __syncthreads();
+  }
+  const int nrows = __builtin_amdgcn_readfirstlane(min(RT, total - rg * RT));
+  if (nrows <= 0) return;
+  if (tid < RT && tid >= nrows) g_rows[tid] = g_rows[0];
+  __syncthreads();
+
+  // ---- copy offsets (fixed per lane; the stage moves the scalar bases by 128 bytes)
+  const size_t rowb = (size_t)a.K * 2;
+  uint32_t woff[WDMA], hoff[HDMA];
+#pragma unroll
+  for (int i = 0; i < WDMA; ++i) {
+    const int row = (wave * WDMA + i) * 8 + (lane >> 3);
+    const int vrow = min(vt * VT + row, a.V - 1) - vt * VT;  // rows past V read the last row
+    woff[i] = (uint32_t)((size_t)vrow * rowb) + ((((lane & 7) ^ swz(row))) << 4);
+  }
+#pragma unroll
+  for (int j = 0; j < HDMA; ++j) {
+    const int row = (wave * HDMA + j) * 8 + (lane >> 3);
+    hoff[j] = (uint32_t)((size_t)g_rows[row] * rowb) + ((((lane & 7) ^ swz(row))) << 4);
+  }
+  const char* wbase = uniform_ptr(static_cast<const char*>(a.weight) + (size_t)vt * VT * rowb);
+  const char* hbase = uniform_ptr(static_cast<const char*>(a.hidden));
+  const uint32_t lds0 = lds_addr(g_lds);
+
+  auto issue = [&](int s) {
+    const int q = s % NSTG;
+    const char* wb = wbase + (size_t)s * ROWB;
+    const char* hb = hbase + (size_t)s * ROWB;
+    const uint32_t ls = lds0 + q * STB;
+#pragma unroll
+    for (int i = 0; i < WDMA; ++i) dma16u(wb, woff[i], ls + (wave * WDMA + i) * 1024);
+#pragma unroll
+    for (int j = 0; j < HDMA; ++j) dma16u(hb, hoff[j], ls + WTB + (wave * HDMA + j) * 1024);
+  };
+
+  // ---- operand read offsets: wave (wr, wv) holds rows wr*64.. and vocabulary wv*64..
+  const int wr = wave & 1, wv = wave >> 1;
+  const int lr = lane & 31, lh = lane >> 5;
+  int offA[KS / 16], offB[KS / 16];
+  {
+    const int ra = wv * 64 + lr, rb = wr * 64 + lr;  // +32 for the second block: same swizzle
+#pragma unroll
+    for (int ks = 0; ks < KS / 16; ++ks) {
+      offA[ks] = ra * ROWB + (((2 * ks + lh) ^ swz(ra)) << 4);
+      offB[ks] = WTB + rb * ROWB + (((2 * ks + lh) ^ swz(rb)) << 4);
+    }
+  }
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.0f;
+
+  const int NS = a.K / KS;
+  issue(0);
+  if (NS > 1) issue(1);
+  for (int s = 0; s < NS; ++s) {
+    if (s + 1 < NS) LM_WAIT_VM(DMA_PER_STAGE);  // stage s has landed (this wave's copies)
+    else LM_WAIT_VM(0);
+    __syncthreads();  // every wave's copies of stage s; every wave is done with stage s-1
+    if (s + 2 < NS) issue(s + 2);  // into the slot of stage s-1
+    const char* st = g_lds + (s % NSTG) * STB;
+#pragma unroll
+    for (int ks = 0; ks < KS / 16; ++ks) {
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(st + offA[ks]);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(st + offA[ks] + 32 * ROWB);
+      const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(st + offB[ks]);
+      const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(st + offB[ks] + 32 * ROWB);
+      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc[1][1], 0, 0, 0);
+    }
+  }
+  __syncthreads();  // the ring is reused for the epilogue's partials
+
+  // ---- epilogue. acc[mb][nb][i]: row wr*64 + nb*32 + lr, vocabulary entry
+  // vt*256 + wv*64 + mb*32 + 8*(i/4) + 4*lh + i%4 (increasing in (mb, i)).
+  float* pm = reinterpret_cast<float*>(g_lds);
+  int* pt = reinterpret_cast<int*>(g_lds + RT * 4 * 4);
+  float* pz = reinterpret_cast<float*>(g_lds + RT * 4 * 8);
+  const int v0 = vt * VT + wv * 64 + 4 * lh;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    float m = -INFINITY;
+    int tok = 0x7fffffff;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int v = v0 + mb * 32 + 8 * (i >> 2) + (i & 3);
+        const float x = acc[mb][nb][i];
+        if (v < a.V && x > m) {
+          m = x;
+          tok = v;
+        }
+      }
+    // exp of (x - m): the difference first, so the max term is exactly 1 and each exponent's
+    // rounding is relative to x - m (a scaled m would carry the rounding of m * log2 e)
+    float z = 0.0f;
+    if (m != -INFINITY) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int v = v0 + mb * 32 + 8 * (i >> 2) + (i & 3);
+          if (v < a.V) z += exp2f((acc[mb][nb][i] - m) * kLog2e);
+        }
+    }
+    const float m2 = __shfl_xor(m, 32);
+    const int t2 = __shfl_xor(tok, 32);
+    const float z2 = __shfl_xor(z, 32);
+    part_merge(m, tok, z, m2, t2, z2);
+    if (lh == 0) {
+      const int r = wr * 64 + nb * 32 + lr;
+      pm[r * 4 + wv] = m;
+      pt[r * 4 + wv] = tok;
+      pz[r * 4 + wv] = z;
+    }
+  }
+  __syncthreads();
+  if (tid < nrows) {
+    float m = pm[tid * 4];
+    int tok = pt[tid * 4];
+    double z = pz[tid * 4];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+      const float m2 = pm[tid * 4 + w];
+      if (m2 == -INFINITY) continue;
+      const double z2 = pz[tid * 4 + w];
+      if (m == -INFINITY) {
+        m = m2;
+        tok = pt[tid * 4 + w];
+        z = z2;
+        continue;
+      }
+      const float M = fmaxf(m, m2);
+      z = z * exp((double)m - (double)M) + z2 * exp((double)m2 - (double)M);
+      if (m2 > m) tok = pt[tid * 4 + w];  // equal maxima keep the earlier (lower) block
+      m = M;
+    }
+    CommitChunk c;
+    c.m = m;
+    c.tok = tok;
+    c.z = z;
+    a.chunks[(size_t)g_rows[tid] * a.NVT + vt] = c;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_lmhead_reduce(const LmHeadArgs& a, hipStream_t s) {
+  const int groups = (a.NVT + 7) / 8;
+  hipLaunchKernelGGL(lmhead_reduce_kernel, dim3(8 * a.NRG * groups), dim3(NTHR), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace tt

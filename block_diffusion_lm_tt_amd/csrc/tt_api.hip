@@ -63,6 +63,22 @@ tt_status plan_commit(int32_t B, int32_t S, int32_t V, int32_t dtype, CommitPlan
   return TT_OK;
 }
 
+struct LmPlan {
+  int NRG, NVT;
+  size_t chunk_bytes;
+};
+
+tt_status plan_lmhead(int32_t B, int32_t S, int32_t K, int32_t V, LmPlan* p) {
+  if (B < 0 || S < 1 || K < 1 || V < 1) return TT_ERR_INVALID_ARG;
+  if (S > 1024 || (long long)B * S > kLmMaxRows) return TT_ERR_UNSUPPORTED;
+  if (K % kLmFeaturesPerStage != 0 || K > (1 << 20)) return TT_ERR_UNSUPPORTED;
+  if ((long long)B * S * K >= (1LL << 31)) return TT_ERR_UNSUPPORTED;
+  p->NRG = (B * S + kLmRowsPerWg - 1) / kLmRowsPerWg;
+  p->NVT = (int)(((long long)V + kLmVocabPerWg - 1) / kLmVocabPerWg);
+  p->chunk_bytes = align_up((size_t)B * S * p->NVT * sizeof(CommitChunk));
+  return TT_OK;
+}
+
 // ---- timing -------------------------------------------------------------------------
 constexpr int kMaxTimed = 4096;
 
@@ -71,8 +87,9 @@ struct Profiler {
   bool enabled = false;
   std::vector<hipEvent_t> attn_ev[4];   // attn start, main start, main end, attn end
   std::vector<hipEvent_t> commit_ev[3]; // commit start, reduce end, commit end
-  int64_t attn_calls = 0, commit_calls = 0;
-  int attn_used = 0, commit_used = 0;
+  std::vector<hipEvent_t> lm_ev[3];     // LM-head commit start, reduce end, end
+  int64_t attn_calls = 0, commit_calls = 0, lm_calls = 0;
+  int attn_used = 0, commit_used = 0, lm_used = 0;
 };
 Profiler g_prof;
 
@@ -223,6 +240,73 @@ tt_status tt_commit(int32_t B, int32_t S, int32_t V, int32_t dtype, const void* 
   return e == hipSuccess ? TT_OK : TT_ERR_HIP;
 }
 
+size_t tt_lmhead_commit_workspace(int32_t B, int32_t S, int32_t K, int32_t V) {
+  LmPlan p;
+  if (plan_lmhead(B, S, K, V, &p) != TT_OK) return 0;
+  return p.chunk_bytes < kAlign ? kAlign : p.chunk_bytes;
+}
+
+tt_status tt_lmhead_commit(int32_t B, int32_t S, int32_t K, int32_t V, const void* hidden,
+                           const void* weight, const uint8_t* mask, float gamma,
+                           int32_t* token_id, uint8_t* committed, float* conf, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  LmPlan p;
+  tt_status st = plan_lmhead(B, S, K, V, &p);
+  if (st != TT_OK) return st;
+  if (isnan(gamma)) return TT_ERR_INVALID_ARG;
+  if (B == 0) return TT_OK;
+  if (!hidden || !weight || !mask || !token_id || !committed) return TT_ERR_INVALID_ARG;
+  const size_t need = tt_lmhead_commit_workspace(B, S, K, V);
+  if (!workspace || workspace_bytes < need) return TT_ERR_WORKSPACE;
+
+  LmHeadArgs l;
+  l.hidden = hidden;
+  l.weight = weight;
+  l.mask = mask;
+  l.chunks = static_cast<CommitChunk*>(workspace);
+  l.B = B;
+  l.S = S;
+  l.K = K;
+  l.V = V;
+  l.NRG = p.NRG;
+  l.NVT = p.NVT;
+
+  CommitArgs c;
+  c.logits = nullptr;  // decisions on the chunk estimates (the logits are never stored)
+  c.mask = mask;
+  c.gamma = gamma;
+  c.token_id = token_id;
+  c.committed = committed;
+  c.conf = conf;
+  c.chunks = l.chunks;
+  c.B = B;
+  c.S = S;
+  c.V = V;
+  c.n_chunks = p.NVT;
+  c.chunk_elems = kLmVocabPerWg;
+  c.dtype = TT_BF16;
+
+  hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+  {
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    if (g_prof.enabled) {
+      ++g_prof.lm_calls;
+      if (g_prof.lm_used < kMaxTimed) {
+        for (int k = 0; k < 3; ++k) ev[k] = ev_slot(g_prof.lm_ev[k], g_prof.lm_used);
+        if (ev[0] && ev[1] && ev[2]) ++g_prof.lm_used;
+        else ev[0] = ev[1] = ev[2] = nullptr;
+      }
+    }
+  }
+  if (ev[0]) (void)hipEventRecord(ev[0], stream);
+  hipError_t e = launch_lmhead_reduce(l, stream);
+  if (e != hipSuccess) return TT_ERR_HIP;
+  if (ev[1]) (void)hipEventRecord(ev[1], stream);
+  e = launch_commit_decide(c, stream);
+  if (ev[2]) (void)hipEventRecord(ev[2], stream);
+  return e == hipSuccess ? TT_OK : TT_ERR_HIP;
+}
+
 tt_status tt_ctx_append(const tt_attn_shape* shape, const void* k_new, const void* v_new,
                         void* k_ctx, void* v_ctx, int32_t* ctx_len, int32_t bump, uint8_t* skipped,
                         hipStream_t stream) {
@@ -261,8 +345,8 @@ tt_status tt_profile_enable(int32_t enable) {
 
 tt_status tt_profile_reset(void) {
   std::lock_guard<std::mutex> lk(g_prof.mu);
-  g_prof.attn_calls = g_prof.commit_calls = 0;
-  g_prof.attn_used = g_prof.commit_used = 0;
+  g_prof.attn_calls = g_prof.commit_calls = g_prof.lm_calls = 0;
+  g_prof.attn_used = g_prof.commit_used = g_prof.lm_used = 0;
   return TT_OK;
 }
 
@@ -285,8 +369,16 @@ tt_status tt_profile_read(tt_profile_stats* out) {
     if (hipEventElapsedTime(&ms, g_prof.commit_ev[0][k], g_prof.commit_ev[1][k]) != hipSuccess) return TT_ERR_HIP;
     s.commit_reduce_ms += ms;
   }
+  for (int k = 0; k < g_prof.lm_used; ++k) {
+    if (hipEventSynchronize(g_prof.lm_ev[2][k]) != hipSuccess) return TT_ERR_HIP;
+    if (hipEventElapsedTime(&ms, g_prof.lm_ev[0][k], g_prof.lm_ev[2][k]) != hipSuccess) return TT_ERR_HIP;
+    s.lm_total_ms += ms;
+    if (hipEventElapsedTime(&ms, g_prof.lm_ev[0][k], g_prof.lm_ev[1][k]) != hipSuccess) return TT_ERR_HIP;
+    s.lm_reduce_ms += ms;
+  }
   s.attn_calls = g_prof.attn_used;
   s.commit_calls = g_prof.commit_used;
+  s.lm_calls = g_prof.lm_used;
   *out = s;
   return TT_OK;
 }

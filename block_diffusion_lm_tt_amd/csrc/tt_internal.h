@@ -93,5 +93,28 @@ hipError_t launch_ctx_append(const AppendArgs& a, hipStream_t s);
 
 int commit_chunk_elems(int dtype);
 hipError_t launch_commit(const CommitArgs& a, hipStream_t s, hipEvent_t ev_reduce0, hipEvent_t ev_reduce1);
+// the decide step alone (a.logits == nullptr: decisions on the chunk estimates only)
+hipError_t launch_commit_decide(const CommitArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------------------------------
+// LM head fused with the commit's vocabulary reduction
+// ---------------------------------------------------------------------------------------
+
+constexpr int kLmVocabPerWg = 256;      // head rows (vocabulary entries) per workgroup = chunk
+constexpr int kLmRowsPerWg = 128;       // masked hidden rows per workgroup
+constexpr int kLmFeaturesPerStage = 64; // K per LDS stage (K must be a multiple)
+constexpr int kLmMaxRows = 4096;        // B*S limit
+
+struct LmHeadArgs {
+  const void* hidden;   // [B*S][K] bf16
+  const void* weight;   // [V][K] bf16
+  const uint8_t* mask;  // [B*S]
+  CommitChunk* chunks;  // [B*S][NVT]
+  int B, S, K, V;
+  int NRG;              // row groups: ceil(B*S / 128)
+  int NVT;              // vocabulary tiles: ceil(V / 256)
+};
+
+hipError_t launch_lmhead_reduce(const LmHeadArgs& a, hipStream_t s);
 
 }  // namespace tt

@@ -25,3 +25,10 @@ def attn_to_device(x: W.AttnInputs, device):
 def commit_to_device(c: W.CommitInputs, device):
     import torch
     return to_torch(c.logits, c.dtype, device), torch.from_numpy(np.ascontiguousarray(c.mask)).to(device)
+
+
+def lmhead_to_device(x: W.LmHeadInputs, device):
+    """(hidden bf16 [B,S,K], weight bf16 [V,K], mask uint8 [B,S]) on the device."""
+    import torch
+    return (to_torch(x.hidden, W.BF16, device), to_torch(x.weight, W.BF16, device),
+            torch.from_numpy(np.ascontiguousarray(x.mask)).to(device))

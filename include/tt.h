@@ -130,6 +130,45 @@ tt_status tt_commit(int32_t B, int32_t S, int32_t V, int32_t dtype, const void *
                     float *conf, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------
+ * tt_lmhead_commit -- the LM head and the confidence commit of one denoising step, fused:
+ * the logits are never written to memory.
+ *
+ * Defined by Nemotron-TwoTower (gist.science explainer), Technical Summary > Training and
+ * Conditioning > Sampling (every masked token is predicted at once from the denoiser's
+ * output; those whose confidence is above gamma are committed) and the snilld.dk TwoTower
+ * article, "Blockwise generering i praksis". The prediction's last step is the LM head: for
+ * every masked position (b,i),
+ *   l[b,i,v] = sum_k hidden[b,i,k] * weight[v,k]     (bf16 inputs, fp32 accumulation,
+ *                                                      summation order unspecified)
+ * and then the rule of tt_commit on these fp32 logits: token = lowest v attaining the max,
+ * Z = sum_v exp(l_v - max), conf = 1/Z, committed = conf > gamma, and the fallback to the
+ * most confident masked position (lowest i on ties) of a sequence that commits nothing.
+ * Unlike tt_commit there is no exact recomputation near the threshold (there are no stored
+ * logits to recompute from): the decisions are taken on the fp32 logits and an fp64 merge
+ * of fp32 partial sums of exp. The logits themselves carry the fp32 accumulation error,
+ * at most K * 2^-24 * sum_k |hidden[b,i,k] * weight[v,k]| per logit.
+ *
+ *   hidden     [B, S, K]   bf16 (device, read: masked rows only)
+ *   weight     [V, K]      bf16 (device, read), the head's rows, one per vocabulary entry
+ *   mask       [B, S]      uint8, nonzero = masked (device, read)
+ *   gamma      any non-NaN value
+ *   token_id   [B, S]      int32 (device, written; -1 at unmasked positions)
+ *   committed  [B, S]      uint8 (device, written)
+ *   conf       [B, S]      float, may be NULL (device, written; 0 at unmasked positions)
+ *   workspace  device memory of tt_lmhead_commit_workspace(B, S, K, V) bytes (16 bytes per
+ *              position and 256-entry vocabulary chunk); contents on entry are ignored
+ *
+ * Supported: K a multiple of 64 (at most 2^20); 1 <= S <= 1024; B*S <= 4096;
+ * B*S*K < 2^31; any V >= 1. Anything else returns TT_ERR_UNSUPPORTED. B == 0 is a no-op.
+ * ------------------------------------------------------------------------------------- */
+size_t tt_lmhead_commit_workspace(int32_t B, int32_t S, int32_t K, int32_t V);
+
+tt_status tt_lmhead_commit(int32_t B, int32_t S, int32_t K, int32_t V, const void *hidden,
+                           const void *weight, const uint8_t *mask, float gamma,
+                           int32_t *token_id, uint8_t *committed, float *conf, void *workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------
  * tt_ctx_append -- context cache update after a block is committed.
  *
  * Defined by Nemotron-TwoTower (gist.science explainer), Technical Summary > Generation
@@ -173,6 +212,9 @@ typedef struct {
     int64_t commit_calls;     /* tt_commit calls timed                                   */
     double commit_total_ms;   /* sum over those calls, first launch to last              */
     double commit_reduce_ms;  /* sum over those calls, the vocabulary reduction kernel   */
+    int64_t lm_calls;         /* tt_lmhead_commit calls timed                            */
+    double lm_total_ms;       /* sum over those calls, first launch to last              */
+    double lm_reduce_ms;      /* sum over those calls, the fused head + reduction kernel */
 } tt_profile_stats;
 
 tt_status tt_profile_enable(int32_t enable);

@@ -104,6 +104,29 @@ def test_commit_validation():
     assert call(args(B=0, lg=None)) == 0
 
 
+def test_lmhead_commit_validation():
+    L = tt.lib()
+    need = L.tt_lmhead_commit_workspace(32, 16, 4096, 131072)
+    assert need == 32 * 16 * 512 * 16  # one 16-byte record per position and 256-entry chunk
+    assert L.tt_lmhead_commit_workspace(1, 1, 100, 10) == 0    # K not a multiple of 64
+    assert L.tt_lmhead_commit_workspace(1, 0, 64, 10) == 0
+    assert L.tt_lmhead_commit_workspace(5, 1000, 64, 10) == 0  # B*S > 4096
+    args = lambda **kw: dict(dict(B=32, S=16, K=4096, V=131072, h=FAKE, w=FAKE, mk=FAKE, g=0.8,  # noqa
+                                  tok=FAKE, com=FAKE, conf=None, ws=FAKE, n=need), **kw)
+    call = lambda a: L.tt_lmhead_commit(a["B"], a["S"], a["K"], a["V"], a["h"], a["w"], a["mk"],  # noqa
+                                        a["g"], a["tok"], a["com"], a["conf"], a["ws"], a["n"], None)
+    assert call(args(g=float("nan"))) == INVALID
+    for kw in (dict(S=0), dict(K=0), dict(V=0), dict(B=-1)):
+        assert call(args(**kw)) == INVALID
+    for kw in (dict(K=100), dict(S=1025), dict(B=300), dict(K=1 << 21)):
+        assert call(args(**kw)) == UNSUPPORTED
+    for k in ("h", "w", "mk", "tok", "com"):
+        assert call(args(**{k: None})) == INVALID
+    assert call(args(n=need - 1)) == WORKSPACE
+    assert call(args(ws=None)) == WORKSPACE
+    assert call(args(B=0, h=None, w=None)) == 0
+
+
 @pytest.mark.parametrize("kw,want", [
     (dict(S=0), INVALID), (dict(B=-1), INVALID), (dict(Hkv=0), INVALID), (dict(D=0), INVALID),
     (dict(Lmax=-1), INVALID), (dict(dtype=7), UNSUPPORTED), (dict(D=300), UNSUPPORTED),
@@ -129,7 +152,7 @@ def test_profile_api_without_gpu_work():
     tt.profile_enable(True)
     tt.profile_reset()
     st = tt.profile_read()
-    assert st["attn_calls"] == 0 and st["commit_calls"] == 0
+    assert st["attn_calls"] == 0 and st["commit_calls"] == 0 and st["lm_calls"] == 0
     tt.profile_enable(False)
 
 
