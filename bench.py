@@ -208,6 +208,121 @@ def loop_bench(w, args, torch, tt, TZ, W):
     print(json.dumps(res), flush=True)
 
 
+def lmhead_bench(args, torch, tt, TZ, W):
+    """The LM head fused with the commit (tt_lmhead_commit) on the batched-serving commit
+    workload's positions: B=32, S=16, 4..16 masked positions per sequence, V=131072, with
+    d_model K = Hq * D = 4096; hidden states N(0,1), head rows N(0, 3/sqrt(K)) (logits of
+    standard deviation about 3) and token peaks of +8..+14 at 60% of the positions. Timed
+    beside it: the unfused pair a plain pipeline would run (the head as one library GEMM over
+    all B*S positions writing bf16 logits, then tt_commit), and the library GEMM over the
+    masked rows alone. Prints one JSON line (an extra line, not the headline)."""
+    dev = torch.device("cuda:0")
+    w3 = W.WORKLOADS[3]
+    K = w3.Hq * w3.D
+    log(f"[lmhead] generating B={w3.B} S={w3.S} K={K} V={w3.V}")
+    x = W.make_lmhead(w3.B, w3.S, K, w3.V, seed=w3.seed, gamma=w3.gamma,
+                      mask=W.random_mask(w3.B, w3.S, 4, 16, seed=w3.seed),
+                      peaks={"p": 0.6, "low": 8.0, "high": 14.0})
+    h, wt, mk = TZ.lmhead_to_device(x, dev)
+    R = int(x.mask.sum())
+    ws = torch.empty(tt.tt_lmhead_commit_workspace(x.B, x.S, K, x.V), dtype=torch.uint8, device=dev)
+    tok = torch.empty((x.B, x.S), dtype=torch.int32, device=dev)
+    com = torch.empty((x.B, x.S), dtype=torch.uint8, device=dev)
+    conf = torch.empty((x.B, x.S), dtype=torch.float32, device=dev)
+
+    def fused():
+        tt.tt_lmhead_commit(h, wt, mk, x.gamma, token_id=tok, committed=com, conf=conf, workspace=ws)
+
+    def timed(fn, reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    reps = max(5, args.steps // 2)
+    for _ in range(max(2, args.warmup // 2)):
+        fused()
+    tt.profile_enable(True)
+    tt.profile_reset()
+    t_events = timed(fused, reps)
+    prof = tt.profile_read()
+    tt.profile_enable(False)
+    t_reduce = prof["lm_reduce_ms"] / max(1, prof["lm_calls"]) * 1e-3
+    t_call = timed(fused, reps)
+
+    h2 = h.reshape(-1, K)
+    idx = torch.from_numpy(np.nonzero(x.mask.reshape(-1))[0]).to(dev)
+    hm = h2.index_select(0, idx).contiguous()
+    ws_c = torch.empty(tt.tt_commit_workspace(x.B, x.S, x.V, 1), dtype=torch.uint8, device=dev)
+    tok2, com2 = torch.empty_like(tok), torch.empty_like(com)
+
+    def unfused():
+        lg = torch.nn.functional.linear(h2, wt).reshape(x.B, x.S, x.V)
+        tt.tt_commit(lg, mk, x.gamma, token_id=tok2, committed=com2, want_conf=False, workspace=ws_c)
+
+    def gemm_masked():
+        torch.nn.functional.linear(hm, wt)
+
+    for _ in range(2):
+        unfused()
+        gemm_masked()
+    t_unfused = timed(unfused, reps)
+    t_gemm = timed(gemm_masked, reps)
+    mb = mk.bool()
+    agree = float((tok[mb] == tok2[mb]).double().mean().item()) if R else 1.0  # bf16 logits round
+    log(f"[lmhead] fused {t_call*1e6:.1f} us/call (kernel {t_reduce*1e6:.1f} us), unfused "
+        f"{t_unfused*1e6:.1f} us, library GEMM over the {R} masked rows {t_gemm*1e6:.1f} us; "
+        f"tokens equal to the unfused pair (bf16 logits) at {100 * agree:.1f}% of masked positions")
+
+    wbytes = x.V * K * 2
+    alg_bytes = wbytes + R * K * 2
+    flops = 2.0 * R * x.V * K
+    gbs = alg_bytes / t_reduce / 1e9
+    tfl = flops / t_reduce / 1e12
+    bound = "hbm" if gbs / HBM_PEAK_GBS >= tfl / MFMA_BF16_PEAK_TFLOPS else "mfma"
+    roof = ({"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS}
+            if bound == "hbm" else
+            {"bound": "mfma", "achieved": tfl, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+             "frac": tfl / MFMA_BF16_PEAK_TFLOPS})
+    roof.update({"kernel": "lmhead_reduce_kernel", "traffic": None, "avg_us": t_reduce * 1e6,
+                 "algorithmic_bytes_per_launch": alg_bytes, "algorithmic_flop_per_launch": flops,
+                 "hbm_frac": gbs / HBM_PEAK_GBS, "mfma_frac": tfl / MFMA_BF16_PEAK_TFLOPS})
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import ttref_lmhead_commit, ttref_threads
+        done, t_total, b = 0, 0.0, 0
+        budget = min(args.cpu_budget, 15.0)
+        while t_total < budget and b < x.B:
+            sub = (np.ascontiguousarray(x.hidden[b:b + 1]), np.ascontiguousarray(x.mask[b:b + 1]))
+            t0 = time.perf_counter()
+            ttref_lmhead_commit(1, x.S, K, x.V, sub[0], x.weight, sub[1], x.gamma)
+            t_total += time.perf_counter() - t0
+            done += int(x.mask[b].sum())
+            b += 1
+        cpu = {"value": done / t_total, "unit": "masked positions/s", "cores": ttref_threads(),
+               "kind": "oracle",
+               "sample": f"the first {b} sequences of the batch ({done} masked positions), {t_total:.1f} s"}
+        log(f"[lmhead] cpu baseline {cpu['value']:.2f} positions/s on {cpu['cores']} threads")
+    res = {"metric": "fused LM head + commit: masked positions decided per second", "unit": "positions/s",
+           "value": R / t_call, "n_gpus": 1, "steps": reps, "warmup": max(2, args.warmup // 2),
+           "ms_per_step": t_call * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16", "data": "synthetic (seeded; N(0,1) hidden states, N(0,3/sqrt(K)) head rows, "
+                                    "token peaks)",
+           "config": {"workload": f"LM head + commit behind {w3.name}", "B": x.B, "S": x.S, "K": K,
+                      "V": x.V, "masked_positions": R, "gamma": x.gamma},
+           "lmhead_commit_us_per_call": t_call * 1e6,
+           "lmhead_commit_us_per_call_with_timing_events": t_events * 1e6,
+           "unfused_library_gemm_all_rows_plus_tt_commit_us": t_unfused * 1e6,
+           "library_gemm_masked_rows_us": t_gemm * 1e6,
+           "token_agreement_with_unfused_bf16_logits": agree,
+           "roofline": roof, "cpu_baseline": cpu}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -220,6 +335,8 @@ def main():
                          "not the headline)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work sampled")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--lmhead", action="store_true",
+                    help="the fused LM head + commit line instead (an extra line, not the headline)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -246,6 +363,9 @@ def main():
     w = W.WORKLOADS[args.config]
     if args.block_size:
         w = dataclasses.replace(w, S=args.block_size, name=f"{w.name} (block size S={args.block_size})")
+    if args.lmhead:
+        lmhead_bench(args, torch, tt, TZ, W)
+        return
     if w.layers != 1:
         loop_bench(w, args, torch, tt, TZ, W)
         return

@@ -17,12 +17,14 @@
 //    the head rows on the M side and the hidden rows on the N side (C^T = W H^T): both
 //    operands are 16-byte row-major reads of K-contiguous rows. fp32 accumulators stay in
 //    registers for the whole K loop.
-//  * K runs in stages of 64 features. A stage (32 KB of head rows + 16 KB of hidden rows)
-//    goes HBM -> LDS directly (global_load_lds_dwordx4, six 1-KB copies per wave) into a
-//    ring of 3 stages: two in flight while one is read; one barrier per stage. Each
-//    128-byte LDS row holds its eight 16-byte chunks permuted by slot = chunk ^ ((row/2)%8)
-//    (applied on the global side of the copy), so the 16 lanes of one ds_read_b128 pass
-//    (16 consecutive rows, one chunk) hit 16 distinct bank groups.
+//  * K runs in stages of 64 features (32 KB of head rows + 16 KB of hidden rows). The
+//    loads run four stages ahead into registers (six 16-byte loads per lane per stage,
+//    96 VGPRs in flight, about 2 us of matrix work: HBM latency under load is well past
+//    what a three-stage LDS ring of 48 KB stages covers); each stage then goes from
+//    registers into one of two LDS buffers (ds_write_b128, 1 KB per wave per load); one
+//    barrier per stage. Each 128-byte LDS row holds its eight 16-byte chunks permuted by
+//    slot = chunk ^ ((row/2)%8) (applied on the global side), so the 16 lanes of one
+//    ds_read_b128 pass (16 consecutive rows, one chunk) hit 16 distinct bank groups.
 //  * The masked rows are compacted inside the kernel (a ballot scan of the mask by every
 //    workgroup), so the launch needs no host synchronisation; a row group past the number
 //    of masked rows exits at once, and the last group pads with its first row (results
@@ -33,7 +35,8 @@
 //  * Epilogue: each lane holds 32 logits of one row; a lane scans them in increasing
 //    vocabulary order (max, lowest argmax), sums exp relative to its max, merges with the
 //    lane holding the row's other 32 (lanes l, l^32), and the four waves of a row merge
-//    through LDS in vocabulary order into the chunk record (z widened to fp64).
+//    through LDS in vocabulary order into the chunk record (z widened to fp64). A second
+//    launch merges each masked row's chunk records (one workgroup per row) into one.
 #include "tt_internal.h"
 
 namespace tt {
@@ -41,6 +44,8 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const u32x4 gu32x4;  // global memory: no flat loads
 
 constexpr int VT = kLmVocabPerWg;     // 256 head rows per workgroup
 constexpr int RT = kLmRowsPerWg;      // 128 hidden rows per workgroup
@@ -49,24 +54,22 @@ constexpr int ROWB = KS * 2;          // 128-byte LDS rows
 constexpr int WTB = VT * ROWB;        // 32 KB of head rows per stage
 constexpr int HTB = RT * ROWB;        // 16 KB of hidden rows per stage
 constexpr int STB = WTB + HTB;        // 48 KB per stage
-constexpr int NSTG = 3;
+constexpr int NSTG = 2;               // LDS buffers
 constexpr int NW = 8;
 constexpr int NTHR = NW * 64;
-constexpr int WDMA = WTB / 1024 / NW;  // 4 copies of head rows per wave per stage
-constexpr int HDMA = HTB / 1024 / NW;  // 2 copies of hidden rows per wave per stage
-constexpr int DMA_PER_STAGE = WDMA + HDMA;
+constexpr int WDMA = WTB / 1024 / NW;  // 4 loads of head rows per lane per stage
+constexpr int HDMA = HTB / 1024 / NW;  // 2 loads of hidden rows per lane per stage
+constexpr int NCP = WDMA + HDMA;      // 16-byte loads per lane per stage
+constexpr int P = 4;                  // stages held in registers (loads in flight)
 constexpr float kLog2e = 1.4426950408889634f;
 
 static_assert(RT == 2 * 64 && VT == 4 * 64, "waves: 2 row blocks x 4 vocabulary blocks of 64");
-static_assert(ROWB * 8 == 1024, "one copy = 8 LDS rows");
-static_assert(NSTG * STB <= 160 * 1024 - 8 * 1024, "ring and epilogue fit the LDS");
+static_assert(ROWB * 8 == 1024, "one 16-byte load per lane = 8 LDS rows");
+static_assert(NSTG * STB <= 160 * 1024 - 8 * 1024, "buffers and epilogue fit the LDS");
 
 __shared__ __attribute__((aligned(1024))) char g_lds[NSTG * STB];
 __shared__ int g_rows[RT];
 __shared__ int g_wcnt[NW];
-
-// wait until at most n vector-memory operations of this wave are outstanding (n <= 63)
-#define LM_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x70 | 0xF00)
 
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
@@ -75,20 +78,6 @@ __device__ __forceinline__ const char* uniform_ptr(const char* p) {
   const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
   const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
   return reinterpret_cast<const char*>((uintptr_t)((hi << 32) | lo));
-}
-
-// One global -> LDS copy of 16 bytes per lane from a wave-uniform base plus a 32-bit lane
-// offset; lane i's bytes land at LDS byte lds + 16 i. As asm so that the compiler does not
-// make later LDS reads wait for it; completion is awaited explicitly (vmcnt) before the
-// barrier that publishes a stage. No register result.
-__device__ __forceinline__ void dma16u(const char* base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:0" ::"v"(voff),
-               "s"(base), "s"(lds)
-               : "memory", "m0");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const char* p) {
-  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
 }
 
 // (m, tok, z) merge of two partials over disjoint vocabulary sets: larger max wins, equal
@@ -107,6 +96,8 @@ __device__ __forceinline__ void part_merge(float& m, int& tok, float& z, float m
   m = M;
 }
 
+// STRAIGHT: K is a multiple of 64*P with at least 2P stages (the straight-line schedule).
+template <bool STRAIGHT>
 __global__ __launch_bounds__(NTHR, 1) void lmhead_reduce_kernel(LmHeadArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -143,7 +134,7 @@ __global__ __launch_bounds__(NTHR, 1) void lmhead_reduce_kernel(LmHeadArgs a) {
   if (tid < RT && tid >= nrows) g_rows[tid] = g_rows[0];
   __syncthreads();
 
-  // ---- copy offsets (fixed per lane; the stage moves the scalar bases by 128 bytes)
+  // ---- load offsets (fixed per lane; the stage moves the scalar bases by 128 bytes)
   const size_t rowb = (size_t)a.K * 2;
   uint32_t woff[WDMA], hoff[HDMA];
 #pragma unroll
@@ -159,17 +150,23 @@ __global__ __launch_bounds__(NTHR, 1) void lmhead_reduce_kernel(LmHeadArgs a) {
   }
   const char* wbase = uniform_ptr(static_cast<const char*>(a.weight) + (size_t)vt * VT * rowb);
   const char* hbase = uniform_ptr(static_cast<const char*>(a.hidden));
-  const uint32_t lds0 = lds_addr(g_lds);
 
-  auto issue = [&](int s) {
-    const int q = s % NSTG;
+  // stage s of this wave: 16 bytes per lane per copy, held in registers until written to LDS
+  auto gload = [&](int s, u32x4 (&r)[NCP]) {
     const char* wb = wbase + (size_t)s * ROWB;
     const char* hb = hbase + (size_t)s * ROWB;
-    const uint32_t ls = lds0 + q * STB;
 #pragma unroll
-    for (int i = 0; i < WDMA; ++i) dma16u(wb, woff[i], ls + (wave * WDMA + i) * 1024);
+    for (int i = 0; i < WDMA; ++i) r[i] = *(gu32x4*)(wb + woff[i]);
 #pragma unroll
-    for (int j = 0; j < HDMA; ++j) dma16u(hb, hoff[j], ls + WTB + (wave * HDMA + j) * 1024);
+    for (int j = 0; j < HDMA; ++j) r[WDMA + j] = *(gu32x4*)(hb + hoff[j]);
+  };
+  // this wave's part of a stage into LDS buffer q: copy i lands at rows (wave*WDMA+i)*8..
+  auto lwrite = [&](int q, const u32x4 (&r)[NCP]) {
+    char* ls = g_lds + q * STB + lane * 16;
+#pragma unroll
+    for (int i = 0; i < WDMA; ++i) *reinterpret_cast<u32x4*>(ls + (wave * WDMA + i) * 1024) = r[i];
+#pragma unroll
+    for (int j = 0; j < HDMA; ++j) *reinterpret_cast<u32x4*>(ls + WTB + (wave * HDMA + j) * 1024) = r[WDMA + j];
   };
 
   // ---- operand read offsets: wave (wr, wv) holds rows wr*64.. and vocabulary wv*64..
@@ -193,28 +190,68 @@ __global__ __launch_bounds__(NTHR, 1) void lmhead_reduce_kernel(LmHeadArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.0f;
 
+  // ---- K loop. Before iteration s, LDS buffer s%2 holds stage s (written, not yet
+  // published) and registers rb[(s+1)%P], ... hold stages s+1 .. s+P (loads in flight).
+  // Iteration s: barrier (stage s visible; every wave done with stage s-1's buffer), the
+  // products of stage s, then stage s+1 from registers into the other buffer and the loads
+  // of stage s+1+P into the registers it frees.
   const int NS = a.K / KS;
-  issue(0);
-  if (NS > 1) issue(1);
-  for (int s = 0; s < NS; ++s) {
-    if (s + 1 < NS) LM_WAIT_VM(DMA_PER_STAGE);  // stage s has landed (this wave's copies)
-    else LM_WAIT_VM(0);
-    __syncthreads();  // every wave's copies of stage s; every wave is done with stage s-1
-    if (s + 2 < NS) issue(s + 2);  // into the slot of stage s-1
-    const char* st = g_lds + (s % NSTG) * STB;
+  u32x4 rb[P][NCP];
+  gload(0, rb[0]);
+  lwrite(0, rb[0]);
+#pragma unroll
+  for (int p = 1; p <= P; ++p)
+    if (STRAIGHT || p < NS) gload(p, rb[p % P]);  // (straight: NS >= 2P, no guard)
+  auto iter = [&](int s, u32x4 (&rnext)[NCP], bool write_next, bool load_ahead) {
+    __syncthreads();
+    const char* st = g_lds + (s & 1) * STB;
+    // operands of step ks+1 are read while the products of step ks run
+    bf16x8 op[2][4];
+    auto ld = [&](int ks, bf16x8 (&o)[4]) {
+      o[0] = *reinterpret_cast<const bf16x8*>(st + offA[ks]);
+      o[1] = *reinterpret_cast<const bf16x8*>(st + offA[ks] + 32 * ROWB);
+      o[2] = *reinterpret_cast<const bf16x8*>(st + offB[ks]);
+      o[3] = *reinterpret_cast<const bf16x8*>(st + offB[ks] + 32 * ROWB);
+    };
+    ld(0, op[0]);
 #pragma unroll
     for (int ks = 0; ks < KS / 16; ++ks) {
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(st + offA[ks]);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(st + offA[ks] + 32 * ROWB);
-      const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(st + offB[ks]);
-      const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(st + offB[ks] + 32 * ROWB);
-      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[0][0], 0, 0, 0);
-      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc[0][1], 0, 0, 0);
-      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc[1][0], 0, 0, 0);
-      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc[1][1], 0, 0, 0);
+      if (ks + 1 < KS / 16) ld(ks + 1, op[(ks + 1) & 1]);
+      const bf16x8(&o)[4] = op[ks & 1];
+      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o[0], o[2], acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o[0], o[3], acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o[1], o[2], acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o[1], o[3], acc[1][1], 0, 0, 0);
+    }
+    if (write_next) {
+      lwrite((s + 1) & 1, rnext);
+      if (load_ahead) gload(s + 1 + P, rnext);
+    }
+  };
+  if constexpr (STRAIGHT) {
+    // straight-line blocks of P stages (static register buffers, every load and write
+    // unconditional in the loop, so each wait covers exactly the stage it needs): loads
+    // stop after stage NS-1 (second-to-last block), writes after stage NS-1 (last block)
+    int s = 0;
+    for (; s < NS - 2 * P; s += P) {
+#pragma unroll
+      for (int u = 0; u < P; ++u) iter(s + u, rb[(u + 1) % P], true, true);
+    }
+#pragma unroll
+    for (int u = 0; u < P; ++u) iter(s + u, rb[(u + 1) % P], true, u < P - 1);
+    s += P;
+#pragma unroll
+    for (int u = 0; u < P; ++u) iter(s + u, rb[(u + 1) % P], u < P - 1, false);
+  } else {
+    // any other K: the same schedule with run-time guards (the compiler then waits for every
+    // load in flight before each write)
+    for (int s = 0; s < NS; s += P) {
+#pragma unroll
+      for (int u = 0; u < P; ++u)
+        if (s + u < NS) iter(s + u, rb[(u + 1) % P], s + u + 1 < NS, s + u + 1 + P < NS);
     }
   }
-  __syncthreads();  // the ring is reused for the epilogue's partials
+  __syncthreads();  // the buffers are reused for the epilogue's partials
 
   // ---- epilogue. acc[mb][nb][i]: row wr*64 + nb*32 + lr, vocabulary entry
   // vt*256 + wv*64 + mb*32 + 8*(i/4) + 4*lh + i%4 (increasing in (mb, i)).
@@ -289,11 +326,74 @@ __global__ __launch_bounds__(NTHR, 1) void lmhead_reduce_kernel(LmHeadArgs a) {
   }
 }
 
+// Merge of a masked row's NVT chunk records into one (the decide step then reads one record
+// per row): 256 threads, each merges its chunks (k = t, t + 256, ...) in fp64, then the
+// workgroup merges the threads' partials; larger max wins, equal maxima keep the lower index
+// (an order-free rule), z moves to the common max in fp64.
+constexpr int MT = 256;
+
+__device__ __forceinline__ void merge_d(float& m, int& tok, double& z, float m2, int tok2, double z2) {
+  if (m2 == -INFINITY) return;
+  if (m == -INFINITY) {
+    m = m2;
+    tok = tok2;
+    z = z2;
+    return;
+  }
+  const float M = fmaxf(m, m2);
+  z = z * exp((double)m - (double)M) + z2 * exp((double)m2 - (double)M);
+  if (m2 > m || (m2 == m && tok2 < tok)) tok = tok2;
+  m = M;
+}
+
+__global__ __launch_bounds__(MT) void lmhead_merge_kernel(LmHeadArgs a) {
+  __shared__ float sm[MT / 64];
+  __shared__ int st[MT / 64];
+  __shared__ double sz[MT / 64];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  if (!a.mask[row]) return;
+  const CommitChunk* c = a.chunks + (size_t)row * a.NVT;
+  float m = -INFINITY;
+  int tok = 0x7fffffff;
+  double z = 0.0;
+  for (int k = tid; k < a.NVT; k += MT) merge_d(m, tok, z, c[k].m, c[k].tok, c[k].z);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float m2 = __shfl_xor(m, off);
+    const int t2 = __shfl_xor(tok, off);
+    const double z2 = __shfl_xor(z, off);
+    merge_d(m, tok, z, m2, t2, z2);
+  }
+  if ((tid & 63) == 0) {
+    sm[tid >> 6] = m;
+    st[tid >> 6] = tok;
+    sz[tid >> 6] = z;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < MT / 64; ++w) merge_d(m, tok, z, sm[w], st[w], sz[w]);
+    CommitChunk r;
+    r.m = m;
+    r.tok = tok;
+    r.z = z;
+    a.merged[row] = r;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_lmhead_reduce(const LmHeadArgs& a, hipStream_t s) {
   const int groups = (a.NVT + 7) / 8;
-  hipLaunchKernelGGL(lmhead_reduce_kernel, dim3(8 * a.NRG * groups), dim3(NTHR), 0, s, a);
+  const int NS = a.K / KS;
+  if (NS % P == 0 && NS >= 2 * P)
+    hipLaunchKernelGGL(lmhead_reduce_kernel<true>, dim3(8 * a.NRG * groups), dim3(NTHR), 0, s, a);
+  else
+    hipLaunchKernelGGL(lmhead_reduce_kernel<false>, dim3(8 * a.NRG * groups), dim3(NTHR), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_lmhead_merge(const LmHeadArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(lmhead_merge_kernel, dim3(a.B * a.S), dim3(MT), 0, s, a);
   return hipGetLastError();
 }
 

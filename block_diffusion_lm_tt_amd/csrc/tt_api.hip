@@ -65,7 +65,7 @@ tt_status plan_commit(int32_t B, int32_t S, int32_t V, int32_t dtype, CommitPlan
 
 struct LmPlan {
   int NRG, NVT;
-  size_t chunk_bytes;
+  size_t chunk_bytes, merged_bytes;
 };
 
 tt_status plan_lmhead(int32_t B, int32_t S, int32_t K, int32_t V, LmPlan* p) {
@@ -76,6 +76,7 @@ tt_status plan_lmhead(int32_t B, int32_t S, int32_t K, int32_t V, LmPlan* p) {
   p->NRG = (B * S + kLmRowsPerWg - 1) / kLmRowsPerWg;
   p->NVT = (int)(((long long)V + kLmVocabPerWg - 1) / kLmVocabPerWg);
   p->chunk_bytes = align_up((size_t)B * S * p->NVT * sizeof(CommitChunk));
+  p->merged_bytes = align_up((size_t)B * S * sizeof(CommitChunk));
   return TT_OK;
 }
 
@@ -243,7 +244,7 @@ tt_status tt_commit(int32_t B, int32_t S, int32_t V, int32_t dtype, const void* 
 size_t tt_lmhead_commit_workspace(int32_t B, int32_t S, int32_t K, int32_t V) {
   LmPlan p;
   if (plan_lmhead(B, S, K, V, &p) != TT_OK) return 0;
-  return p.chunk_bytes < kAlign ? kAlign : p.chunk_bytes;
+  return p.chunk_bytes + p.merged_bytes;
 }
 
 tt_status tt_lmhead_commit(int32_t B, int32_t S, int32_t K, int32_t V, const void* hidden,
@@ -264,6 +265,7 @@ tt_status tt_lmhead_commit(int32_t B, int32_t S, int32_t K, int32_t V, const voi
   l.weight = weight;
   l.mask = mask;
   l.chunks = static_cast<CommitChunk*>(workspace);
+  l.merged = reinterpret_cast<CommitChunk*>(static_cast<char*>(workspace) + p.chunk_bytes);
   l.B = B;
   l.S = S;
   l.K = K;
@@ -278,12 +280,12 @@ tt_status tt_lmhead_commit(int32_t B, int32_t S, int32_t K, int32_t V, const voi
   c.token_id = token_id;
   c.committed = committed;
   c.conf = conf;
-  c.chunks = l.chunks;
+  c.chunks = l.merged;
   c.B = B;
   c.S = S;
   c.V = V;
-  c.n_chunks = p.NVT;
-  c.chunk_elems = kLmVocabPerWg;
+  c.n_chunks = 1;
+  c.chunk_elems = V;
   c.dtype = TT_BF16;
 
   hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
@@ -302,6 +304,8 @@ tt_status tt_lmhead_commit(int32_t B, int32_t S, int32_t K, int32_t V, const voi
   hipError_t e = launch_lmhead_reduce(l, stream);
   if (e != hipSuccess) return TT_ERR_HIP;
   if (ev[1]) (void)hipEventRecord(ev[1], stream);
+  e = launch_lmhead_merge(l, stream);
+  if (e != hipSuccess) return TT_ERR_HIP;
   e = launch_commit_decide(c, stream);
   if (ev[2]) (void)hipEventRecord(ev[2], stream);
   return e == hipSuccess ? TT_OK : TT_ERR_HIP;

@@ -110,11 +110,14 @@ struct LmHeadArgs {
   const void* weight;   // [V][K] bf16
   const uint8_t* mask;  // [B*S]
   CommitChunk* chunks;  // [B*S][NVT]
+  CommitChunk* merged;  // [B*S], one record per masked row
   int B, S, K, V;
   int NRG;              // row groups: ceil(B*S / 128)
   int NVT;              // vocabulary tiles: ceil(V / 256)
 };
 
+// the head + reduction kernel (chunk records), and the per-row merge of those into merged[]
 hipError_t launch_lmhead_reduce(const LmHeadArgs& a, hipStream_t s);
+hipError_t launch_lmhead_merge(const LmHeadArgs& a, hipStream_t s);
 
 }  // namespace tt

@@ -156,7 +156,8 @@ tt_status tt_commit(int32_t B, int32_t S, int32_t V, int32_t dtype, const void *
  *   committed  [B, S]      uint8 (device, written)
  *   conf       [B, S]      float, may be NULL (device, written; 0 at unmasked positions)
  *   workspace  device memory of tt_lmhead_commit_workspace(B, S, K, V) bytes (16 bytes per
- *              position and 256-entry vocabulary chunk); contents on entry are ignored
+ *              position and 256-entry vocabulary chunk, plus 16 per position); contents on
+ *              entry are ignored
  *
  * Supported: K a multiple of 64 (at most 2^20); 1 <= S <= 1024; B*S <= 4096;
  * B*S*K < 2^31; any V >= 1. Anything else returns TT_ERR_UNSUPPORTED. B == 0 is a no-op.

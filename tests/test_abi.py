@@ -107,7 +107,7 @@ def test_commit_validation():
 def test_lmhead_commit_validation():
     L = tt.lib()
     need = L.tt_lmhead_commit_workspace(32, 16, 4096, 131072)
-    assert need == 32 * 16 * 512 * 16  # one 16-byte record per position and 256-entry chunk
+    assert need == 32 * 16 * 513 * 16  # 16-byte records: per position and 256-entry chunk, then per position
     assert L.tt_lmhead_commit_workspace(1, 1, 100, 10) == 0    # K not a multiple of 64
     assert L.tt_lmhead_commit_workspace(1, 0, 64, 10) == 0
     assert L.tt_lmhead_commit_workspace(5, 1000, 64, 10) == 0  # B*S > 4096
