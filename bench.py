@@ -208,6 +208,20 @@ def loop_bench(w, args, torch, tt, TZ, W):
     print(json.dumps(res), flush=True)
 
 
+def copy_probe(args, torch, dev):
+    """A plain device-to-device copy of known size inside the profiled process (the reading
+    that calibrates the FETCH_SIZE / WRITE_SIZE counters)."""
+    if not args.copy_probe_mib:
+        return
+    n = args.copy_probe_mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] copy probe: {args.copy_probe_mib} MiB device-to-device copy x3")
+
+
 def lmhead_bench(args, torch, tt, TZ, W):
     """The LM head fused with the commit (tt_lmhead_commit) on the batched-serving commit
     workload's positions: B=32, S=16, 4..16 masked positions per sequence, V=131072, with
@@ -272,6 +286,7 @@ def lmhead_bench(args, torch, tt, TZ, W):
         gemm_masked()
     t_unfused = timed(unfused, reps)
     t_gemm = timed(gemm_masked, reps)
+    copy_probe(args, torch, dev)
     mb = mk.bool()
     agree = float((tok[mb] == tok2[mb]).double().mean().item()) if R else 1.0  # bf16 logits round
     log(f"[lmhead] fused {t_call*1e6:.1f} us/call (kernel {t_reduce*1e6:.1f} us), unfused "
@@ -423,14 +438,7 @@ def main():
     torch.cuda.synchronize()
     t_attn_plain = ea.elapsed_time(eb) * 1e-3 / K_PLAIN
 
-    if args.copy_probe_mib:
-        n = args.copy_probe_mib << 20
-        src = torch.empty(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"[bench] copy probe: {args.copy_probe_mib} MiB device-to-device copy x3")
+    copy_probe(args, torch, dev)
 
     K = args.steps
     t_attn = prof["attn_total_ms"] / max(1, prof["attn_calls"]) * 1e-3
