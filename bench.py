@@ -92,10 +92,41 @@ def cpu_baseline(w, budget_s: float) -> dict:
     full_mean = float(x.ctx_len.mean()) + x.S
     samp_mean = ctx_sum / done + x.S
     rate = done / t_total * (samp_mean / full_mean)
+    # the commit's oracle on the same workload's logits (one pass over the masked rows)
+    from oracle import ttref_commit
+    c = w.commit()
+    t0 = time.perf_counter()
+    ttref_commit(c.B, c.S, c.V, c.dtype, c.logits, c.mask, c.gamma)
+    t_commit = time.perf_counter() - t0
     return {"value": rate, "unit": "blocks/s", "cores": ttref_threads(), "kind": "oracle",
             "sample": f"{done} sequence blocks of the timed workload ({done / x.B:.1f} passes over its "
                       f"{x.B} sequences, sum ctx_len {ctx_sum}), {t_total:.1f} s, rate rescaled to the "
-                      f"batch's mean context length"}
+                      f"batch's mean context length",
+            "host_cpu_count": os.cpu_count(), "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
+            "commit_pass_s": t_commit, "commit_masked_rows": int(c.mask.sum()),
+            "single_thread_blocks_per_s": single_thread_rate(x)}
+
+
+def single_thread_rate(x) -> float:
+    """The attention oracle on one thread (a child process started with OMP_NUM_THREADS=1):
+    the batch's first sequence, rescaled to the batch's mean context length."""
+    import subprocess
+    b = 0
+    code = ("import sys, time; sys.path.insert(0, %r)\n"
+            "from block_diffusion_lm_tt_amd import workloads as W\n"
+            "from oracle import ttref_block_denoise_attn\n"
+            "x = W.WORKLOADS[%d].attn(B=%d)\n"
+            "t0 = time.perf_counter()\n"
+            "ttref_block_denoise_attn(1, x.S, x.Hq, x.Hkv, x.D, x.Lmax, x.dtype, x.q[%d:%d], x.k_blk[%d:%d], "
+            "x.v_blk[%d:%d], x.k_ctx[%d:%d], x.v_ctx[%d:%d], x.ctx_len[%d:%d].copy())\n"
+            "print(time.perf_counter() - t0)\n") % (ROOT, 3, b + 1, b, b + 1, b, b + 1, b, b + 1, b, b + 1,
+                                                      b, b + 1, b, b + 1)
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=600)
+    if r.returncode != 0:
+        return float("nan")
+    t = float(r.stdout.strip().splitlines()[-1])
+    return (float(x.ctx_len[b]) + x.S) / (float(x.ctx_len.mean()) + x.S) / t
 
 
 def loop_bench(w, args, torch, tt, TZ, W):
@@ -206,6 +237,22 @@ def loop_bench(w, args, torch, tt, TZ, W):
            "ctx_append_GBps": append_bytes / append_us / 1e3,
            "sweep": results}
     print(json.dumps(res), flush=True)
+
+
+def stream_read_ceiling(torch, dev) -> float:
+    """A streaming read measured in the same run: a library reduction over 2 GiB of fp32
+    (read once, a scalar written), best of five, in GB/s."""
+    x = torch.ones((1 << 29,), dtype=torch.float32, device=dev)
+    best = 0.0
+    for _ in range(6):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        x.sum()
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, x.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del x
+    return best
 
 
 def copy_probe(args, torch, dev):
@@ -437,6 +484,19 @@ def main():
     eb.record()
     torch.cuda.synchronize()
     t_attn_plain = ea.elapsed_time(eb) * 1e-3 / K_PLAIN
+    # per-call spread: one event between consecutive calls (>= 50 calls)
+    n_dist = max(50, args.steps)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_dist + 1)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for k in range(n_dist):
+        r = k % R
+        tt.tt_block_denoise_attn(q, kb, vb, kcs[r], vcs[r], ctx, out=out, workspace=ws_a)
+        evs[k + 1].record()
+    torch.cuda.synchronize()
+    per_call = np.array([evs[k].elapsed_time(evs[k + 1]) * 1e3 for k in range(n_dist)])
+    p10, p50, p90 = (float(np.percentile(per_call, p)) for p in (10, 50, 90))
+    stream_gbs = stream_read_ceiling(torch, dev)
 
     copy_probe(args, torch, dev)
 
@@ -479,7 +539,10 @@ def main():
                    "masked_positions": int(c.mask.sum()), "rotated_copies": R},
         "context_kv_GBps": gbs_call,
         "context_kv_pct_hbm_peak": 100.0 * gbs_call / HBM_PEAK_GBS,
+        "hbm_stream_read_GBps_measured": stream_gbs,
+        "context_kv_pct_of_measured_stream_read": 100.0 * gbs_call / stream_gbs,
         "attn_us_per_call": t_attn_plain * 1e6,
+        "attn_us_per_call_p10_p50_p90": [p10, p50, p90],
         "attn_us_per_call_with_timing_events": t_attn * 1e6,
         "commit_us_per_call": t_commit * 1e6,
         "commit_GBps": commit_bytes / t_commit / 1e9,

@@ -148,6 +148,25 @@ def test_attn_workload_sampled(dev, cid):
         _assert_attn(got[b:b + 1, :, g * G:(g + 1) * G], want, x.dtype, f"workload {cid} b={b} g={g}")
 
 
+def test_attn_block_loop_every_layer_and_later_steps(dev):
+    # the block-loop workload as the loop runs it: each layer's own context KV with the block
+    # Q/K/V of (step, layer); all 6 layers at step 0 and a seeded sample of later (step, layer)
+    import dataclasses
+    w = W.WORKLOADS[5]
+    rng = np.random.default_rng(w.seed)
+    later = list(zip(rng.integers(1, w.steps, 3).tolist(), rng.integers(0, w.layers, 3).tolist()))
+    G = w.Hq // w.Hkv
+    for t, l in [(0, l) for l in range(w.layers)] + later:
+        _say(f"attn block loop step {t} layer {l}")
+        x = w.attn(step=0, layer=l)
+        q, kb, vb = w.block_qkv(t, l)
+        x = dataclasses.replace(x, q=q, k_blk=kb, v_blk=vb)
+        got = _gpu_attn(x, dev)
+        b, g = (7 * t + 3 * l) % w.B, (t + l) % w.Hkv
+        want = _oracle_attn(_slice_b(x, b, heads=(g, G)))
+        _assert_attn(got[b:b + 1, :, g * G:(g + 1) * G], want, x.dtype, f"block loop t={t} l={l} b={b} g={g}")
+
+
 # ------------------------------------------------------------------------------------------------
 # commit
 # ------------------------------------------------------------------------------------------------
