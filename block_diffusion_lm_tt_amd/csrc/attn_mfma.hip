@@ -694,20 +694,22 @@ __global__ __launch_bounds__(NTHR, 1) void attn_mfma_kernel(AttnArgs a) {
   }
 }
 
-// Merge the partials of every unit that a cluster boundary cut. Workgroup (c, y) reads the
+// Merge the partials of every unit that a cluster boundary cut. Workgroup (y, c) reads the
 // merge record of cluster c (none: it exits) and covers 16 query rows of that unit (16
 // threads x 8 head-dim values per row). The pieces lie in clusters first .. c; they are
 // read eight at a time, all loads in flight together, and merged with a running max.
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   constexpr int PB = 8;
-  const int c_last = bid_x();
+  // grid: (row chunk, cluster): the row chunks of one record are consecutive workgroups, so
+  // they spread over the XCDs (workgroup id % 8) whatever the cluster of the record
+  const int c_last = bid_y();
   // the record was written by the previous kernel: scalar loads, uniform arithmetic
   const c_i32* rec = (c_i32*)(uintptr_t)(a.rec + 4 * c_last);
   const int b = rec[0];
   if (b < 0) return;
   const int g = rec[1], c_first = rec[2] >> 1, first_slot = rec[2] & 1;
   const int rows_unit = a.G * a.S;
-  const int r = bid_y() * 16 + (tid_x() >> 4);
+  const int r = bid_x() * 16 + (tid_x() >> 4);
   if (r >= rows_unit) return;
   const int d = (tid_x() & 15) * 8;
   const int qsl = r / RWG, rw = r - qsl * RWG;
@@ -766,7 +768,7 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s, hipEvent_t ev0, hi
   if (e != hipSuccess) return e;
   if (ev1) (void)hipEventRecord(ev1, s);
   const int rows_unit = a.G * a.S;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(a.NC, (rows_unit + 15) / 16), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((rows_unit + 15) / 16, a.NC), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -35,6 +35,12 @@ tt_status plan_attn(const tt_attn_shape* sh, AttnPlan* p) {
   const int G = sh->Hq / sh->Hkv;
   p->NQ = (G * sh->S + kAttnRowsPerWg - 1) / kAttnRowsPerWg;
   int nc = (kCUs * kWgPerCU) / p->NQ;
+  // a small problem takes fewer clusters, so that its units are not cut into more pieces
+  // than their work warrants: at least kAttnMinTilesPerCluster tiles per cluster when every
+  // context is full (ctx_len lives on the device; Lmax bounds it)
+  const long long tmax = (long long)sh->B * sh->Hkv *
+                         ((sh->Lmax + sh->S + kAttnKeysPerTile - 1) / kAttnKeysPerTile);
+  if (tmax / kAttnMinTilesPerCluster < nc) nc = (int)(tmax / kAttnMinTilesPerCluster);
   nc = nc / 8 * 8;
   p->NC = nc < 8 ? 8 : nc;
   if (p->mfma) {

@@ -15,6 +15,7 @@ namespace tt {
 // ---------------------------------------------------------------------------------------
 
 constexpr int kAttnKeysPerTile = 32;   // keys staged in LDS per pipeline step
+constexpr int kAttnMinTilesPerCluster = 8;  // a small problem takes fewer clusters (host plan)
 constexpr int kAttnWaves = 8;          // waves per workgroup of the MFMA kernel
 constexpr int kAttnRowsPerWave = 32;   // query rows (head-in-group x block position) per wave
 constexpr int kAttnRowsPerWg = kAttnWaves * kAttnRowsPerWave;
