@@ -1,7 +1,8 @@
 /*
  * libtt -- the hot path of one block-wise diffusion decoding step, for AMD Instinct MI355X
  * (gfx950): the denoiser's block attention over its own block KV plus the frozen context
- * tower's same-layer KV, and the confidence-threshold (gamma) commit.
+ * tower's same-layer KV, the confidence-threshold (gamma) commit (on given logits, or fused
+ * behind the LM head), and the context cache update once a block is committed.
  *
  * Method source: "Nemotron-TwoTower: Diffusion Language Modeling with Pretrained
  * Autoregressive Context" (gist.science explainer, English), Technical Summary; and the
