@@ -253,11 +253,13 @@ def make_commit(B: int, S: int, V: int, dtype: str = BF16, sigma: float = 3.0, s
 
 
 def random_mask(B: int, S: int, kmin: int, kmax: int, seed: int, step: int = 0) -> np.ndarray:
-    """Per sequence, k ~ U{kmin..kmax} positions (a seeded subset) are still masked."""
+    """Per sequence, k ~ U{kmin..kmax} positions (a seeded subset) are still masked; both
+    bounds are clamped to S (a block shorter than kmin is wholly masked)."""
     r = _rng(seed, _T_MASK, step)
     m = np.zeros((B, S), dtype=np.uint8)
+    lo, hi = min(kmin, S), min(kmax, S)
     for b in range(B):
-        k = int(r.integers(kmin, kmax + 1))
+        k = int(r.integers(lo, hi + 1))
         m[b, r.choice(S, size=k, replace=False)] = 1
     return m
 
