@@ -71,6 +71,21 @@ def profiled_traffic(kernel: str):
     return int(t.group(1))
 
 
+def profiled_avg_us(kernel: str):
+    """The kernel's average duration in the committed rocprofv3 kernel-trace summary, when
+    that summary was taken on the kernel source built here (else None)."""
+    try:
+        text = open(PROFILE_MD).read()
+    except OSError:
+        return None
+    import re
+    m = re.search(r"attention source sha256\[:16\][^`]*`([0-9a-f]+)`", text)
+    t = re.search(r"\| " + kernel + r" \| \d+ \| ([0-9.]+) \|", text)
+    if not m or not t or m.group(1) != attn_source_hash():
+        return None
+    return float(t.group(1))
+
+
 def cpu_baseline(w, budget_s: float) -> dict:
     """The fp64 oracle as it stands, on this host, on a bounded sample of the workload."""
     from oracle import ttref_block_denoise_attn, ttref_threads
@@ -552,7 +567,9 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs_main / HBM_PEAK_GBS,
                      "traffic": profiled_traffic("attn_mfma_kernel")
                      if args.config == 3 and not args.block_size else None,
-                     "avg_us": t_main * 1e6, "algorithmic_bytes_per_launch": kv_bytes},
+                     "avg_us": t_main * 1e6, "algorithmic_bytes_per_launch": kv_bytes,
+                     "profiled_avg_us": profiled_avg_us("attn_mfma_kernel")
+                     if args.config == 3 and not args.block_size else None},
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
