@@ -366,15 +366,16 @@ __device__ __forceinline__ void vector_phase(WaveState& w, float scale_log2, boo
   }
   // P in bf16 for the PV products; the row sum in fp32 from the unrounded values (plain
   // adds: the dot instructions contend with the other wave's matrix products)
-  float ps0 = 0.0f, ps1 = 0.0f;
+  // (the sums start from the first terms: with IEEE semantics 0 + p is not folded)
+  float ps0, ps1;
 #pragma unroll
   for (int k = 0; k < 16; k += 2) {
     const float p0 = __builtin_amdgcn_exp2f(w.s[k] * scale_log2 - w.m_run);
     const float p1 = __builtin_amdgcn_exp2f(w.s[k + 1] * scale_log2 - w.m_run);
     w.pb[k >> 3][k & 7] = (__bf16)p0;
     w.pb[k >> 3][(k & 7) + 1] = (__bf16)p1;
-    ps0 += p0;
-    ps1 += p1;
+    ps0 = k == 0 ? p0 : ps0 + p0;
+    ps1 = k == 0 ? p1 : ps1 + p1;
   }
   w.l_run += ps0 + ps1;
 }
