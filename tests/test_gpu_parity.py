@@ -148,6 +148,21 @@ def test_attn_workload_sampled(dev, cid):
         _assert_attn(got[b:b + 1, :, g * G:(g + 1) * G], want, x.dtype, f"workload {cid} b={b} g={g}")
 
 
+@pytest.mark.parametrize("dtype,D", [(W.BF16, 128), (W.F32, 64)])
+def test_attn_ctx_len_outside_the_storage_is_clamped(dev, dtype, D):
+    # ctx_len lives on the device, so the kernels clamp it to [0, Lmax]: -5 reads no context
+    # row and Lmax + 100 reads all Lmax of them, exactly like 0 and Lmax
+    import block_diffusion_lm_tt_amd as tt
+    Lmax = 96
+    x = W.make_attn(3, 16, 8, 2, D, [0, Lmax, 37], Lmax=Lmax, dtype=dtype, seed=12)
+    _say(f"attn ctx_len clamp {dtype} D={D}")
+    q, kb, vb, kc, vc, _ = TZ.attn_to_device(x, dev)
+    wild = torch.tensor([-5, Lmax + 100, 37], dtype=torch.int32, device=dev)
+    got = tt.tt_block_denoise_attn(q, kb, vb, kc, vc, wild)
+    torch.cuda.synchronize()
+    _assert_attn(got.double().cpu().numpy(), _oracle_attn(x), dtype, "clamped ctx_len")
+
+
 def test_attn_block_loop_every_layer_and_later_steps(dev):
     # the block-loop workload as the loop runs it: each layer's own context KV with the block
     # Q/K/V of (step, layer); all 6 layers at step 0 and a seeded sample of later (step, layer)
