@@ -85,6 +85,9 @@ ATTN_CASES = [
     ("generic-f32-cfg1", 1, 16, 4, 1, 64, [128], 128, W.F32),
     ("generic-bf16-D64", 2, 8, 8, 2, 64, [40, 300], 300, W.BF16),
     ("generic-f32-D80", 2, 3, 6, 3, 80, [0, 257], 260, W.F32),
+    ("generic-bf16-D256", 2, 4, 4, 2, 256, [33, 150], 150, W.BF16),   # the largest head dim
+    ("generic-f32-D1", 1, 2, 2, 1, 1, [5], 8, W.F32),                 # the smallest
+    ("generic-f32-fp32-D128", 2, 16, 8, 2, 128, [70, 0], 80, W.F32),  # fp32 at the MFMA width
 ]
 
 
