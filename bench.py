@@ -145,96 +145,56 @@ def single_thread_rate(x) -> float:
 
 
 def loop_bench(w, args, torch, tt, TZ, W):
-    """Block loop (the block-loop workload): per block, T denoising steps; each step runs
-    tt_block_denoise_attn on every layer (its own context KV, block Q/K/V drawn per
-    (step, layer)) and then tt_commit on that step's logits; the still-masked set shrinks
-    by the committed positions, and the last step commits whatever is left (the end of a
-    block) and every layer's context cache takes the block's rows (tt_ctx_append, the last
-    layer bumping ctx_len). Each block starts from the workload's context lengths again (the
-    caches have S spare rows past Lmax for the update). Reported per gamma: blocks/s = B /
-    (time of the T steps and the cache update) and the positions committed at each step.
-    Inputs are generated and copied to HBM before timing."""
+    """Block loop (the block-loop workload, block_diffusion_lm_tt_amd/blockloop.py): per
+    block, T denoising steps; each step runs tt_block_denoise_attn on every layer (its own
+    context KV, block Q/K/V drawn per (step, layer)) and then tt_commit on that step's
+    logits; the still-masked set shrinks by the committed positions, the last step commits
+    whatever is left, and every layer's context cache takes the block's rows
+    (tt_ctx_append, the last layer bumping ctx_len). Each block starts from the workload's
+    context lengths again. Reported per gamma: blocks/s = B / (time of the T steps and the
+    cache update), per-block p10/p50/p90 over the timed blocks, and the positions committed
+    at each step. Inputs are generated and copied to HBM before timing."""
+    from block_diffusion_lm_tt_amd.blockloop import BlockLoop
     dev = torch.device("cuda:0")
     T, L = w.steps, w.layers
     log(f"[loop] generating workload {w.cid}: {w.name}")
-    ctx0 = torch.from_numpy(w.ctx_lens()).to(dev)
-    ctx = ctx0.clone()
-    kcs, vcs = [], []
-    for l in range(L):
-        x = w.attn(step=0, layer=l)
-        _, _, _, kc, vc, _ = TZ.attn_to_device(x, dev)
-        # S spare rows past Lmax: room for the committed block's rows
-        kb = torch.empty((w.B, w.Lmax + w.S, w.Hkv, w.D), dtype=kc.dtype, device=dev)
-        vb = torch.empty_like(kb)
-        kb[:, :w.Lmax].copy_(kc)
-        vb[:, :w.Lmax].copy_(vc)
-        kcs.append(kb)
-        vcs.append(vb)
-        del x, kc, vc
-    qkv = [[tuple(TZ.to_torch(a, w.dtype, dev) for a in w.block_qkv(t, l)) for l in range(L)]
-           for t in range(T)]
-    logits = [TZ.commit_to_device(w.commit(step=t), dev)[0] for t in range(T)]
-    out = torch.empty_like(qkv[0][0][0])
-    dt = 1 if w.dtype == W.BF16 else 0
-    ws_a = torch.empty(max(1, tt.tt_block_denoise_attn_workspace(w.B, w.S, w.Hq, w.Hkv, w.D, w.Lmax + w.S, dt)),
-                       dtype=torch.uint8, device=dev)
-    ws_c = torch.empty(max(1, tt.tt_commit_workspace(w.B, w.S, w.V, dt)), dtype=torch.uint8, device=dev)
-    tok = torch.empty((w.B, w.S), dtype=torch.int32, device=dev)
-    com = torch.empty((w.B, w.S), dtype=torch.uint8, device=dev)
-    mask = torch.empty((w.B, w.S), dtype=torch.uint8, device=dev)
-    counts = torch.zeros((T,), dtype=torch.int64, device=dev)
-    ones = torch.ones((w.B, w.S), dtype=torch.uint8, device=dev)
-
-    def block(gamma: float):
-        mask.copy_(ones)
-        ctx.copy_(ctx0)
-        for t in range(T):
-            for l in range(L):
-                q, kb, vb = qkv[t][l]
-                tt.tt_block_denoise_attn(q, kb, vb, kcs[l], vcs[l], ctx, out=out, workspace=ws_a)
-            tt.tt_commit(logits[t], mask, gamma, token_id=tok, committed=com, workspace=ws_c,
-                         want_conf=False)
-            if t == T - 1:
-                com.copy_(mask)  # end of the block: every remaining masked position commits
-            counts[t] += com.sum()
-            mask.sub_(com)  # committed positions are masked ones: mask & ~committed
-        # the committed block's rows enter every layer's context cache (stand-in rows: the
-        # last step's block K/V of that layer); the last layer bumps ctx_len
-        for l in range(L):
-            _, kb, vb = qkv[T - 1][l]
-            tt.tt_ctx_append(kb, vb, kcs[l], vcs[l], ctx, bump=(l == L - 1))
+    bl = BlockLoop(w, dev)
 
     results = []
-    reps = max(1, args.steps // 10)
+    reps = max(20, args.steps // 2)
     for gamma in (0.5, 0.8, 0.95):
-        for _ in range(max(1, args.warmup // 10)):
-            block(gamma)
+        for _ in range(max(2, args.warmup // 5)):
+            bl.run_block(gamma)
         torch.cuda.synchronize()
-        counts.zero_()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            block(gamma)
-        e1.record()
+        bl.counts.zero_()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        evs[0].record()
+        for k in range(reps):
+            bl.run_block(gamma)
+            evs[k + 1].record()
         torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / reps
-        per_step = (counts.double() / reps / w.B).tolist()
+        per = np.array([evs[k].elapsed_time(evs[k + 1]) for k in range(reps)])
+        ms = evs[0].elapsed_time(evs[reps]) / reps
+        p10, p50, p90 = (float(np.percentile(per, p)) for p in (10, 50, 90))
+        per_step = (bl.counts.double() / reps / w.B).tolist()
         results.append({"gamma": gamma, "blocks_per_s": w.B / (ms * 1e-3), "ms_per_block": ms,
+                        "ms_per_block_p10_p50_p90": [p10, p50, p90],
                         "tokens_per_step_per_sequence": per_step,
                         "threshold_commits_per_sequence": sum(per_step[:-1]),
                         "end_of_block_commits_per_sequence": per_step[-1]})
-        log(f"[loop] gamma {gamma}: {ms:.3f} ms per block of {T} steps x {L} layers, "
-            f"{w.B / (ms * 1e-3):.1f} blocks/s, committed per step per sequence {per_step}")
+        log(f"[loop] gamma {gamma}: {ms:.3f} ms per block of {T} steps x {L} layers "
+            f"(p10/p50/p90 {p10:.3f}/{p50:.3f}/{p90:.3f}), {w.B / (ms * 1e-3):.1f} blocks/s, "
+            f"committed per step per sequence {per_step}")
     # the cache update alone: L layer calls, timed back-to-back
     reps_a = 20
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
     for _ in range(reps_a):
-        ctx.copy_(ctx0)
+        bl.ctx.copy_(bl.ctx0)
         for l in range(L):
-            _, kb, vb = qkv[T - 1][l]
-            tt.tt_ctx_append(kb, vb, kcs[l], vcs[l], ctx, bump=(l == L - 1))
+            _, kb, vb = bl.qkv[T - 1][l]
+            tt.tt_ctx_append(kb, vb, bl.kcs[l], bl.vcs[l], bl.ctx, bump=(l == L - 1))
     e1.record()
     torch.cuda.synchronize()
     append_us = e0.elapsed_time(e1) * 1e3 / (reps_a * L)

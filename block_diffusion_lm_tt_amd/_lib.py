@@ -14,7 +14,7 @@ import re
 from typing import Optional, Tuple
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.environ.get("TT_LIB", os.path.join(HERE, "libtt.so"))  # TT_LIB: another build of libtt
+LIB_PATH = os.path.join(HERE, "libtt.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "tt.h")
 
 TT_F32, TT_BF16 = 0, 1
@@ -53,9 +53,19 @@ def lib() -> ctypes.CDLL:
             raise ImportError(f"libtt.so not found at {LIB_PATH}; build it first "
                               "(python -c 'import __graft_entry__ as g; g.build()')")
         L = ctypes.CDLL(LIB_PATH)
+        L.tt_build_id.restype = ctypes.c_char_p
+        L.tt_build_id.argtypes = []
+        built = L.tt_build_id().decode()
+        from .build import source_hash
+        want = source_hash()
+        if built != want:  # a stale library is never run
+            raise ImportError(f"libtt.so at {LIB_PATH} was built from other sources (build id "
+                              f"{built}, sources {want}); rebuild it "
+                              "(python -c 'import __graft_entry__ as g; g.build()')")
         vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
         L.tt_version.restype = i32
         L.tt_version.argtypes = []
+        L.build_id = built
         L.tt_status_str.restype = ctypes.c_char_p
         L.tt_status_str.argtypes = [i32]
         L.tt_ctx_append.restype = i32

@@ -6,25 +6,32 @@
 // Z = sum_v exp(l_v - max), conf = 1/Z, committed = conf > gamma; a sequence with masked
 // positions and no commit commits its most confident masked position (lowest i on ties).
 //
-// How: the work is one pass over the masked rows' logits, so it is HBM bound. Two
-// launches, with no communication between workgroups inside a launch:
-//  1. commit_reduce: one workgroup per (masked row, vocabulary chunk). Each thread issues its
-//     eight 16-byte non-temporal loads at once and consumes them in element order with an
-//     online max, lowest argmax and sum of exp2((x - m) * log2 e) relative to its running
-//     max m (rescaled when m grows); the workgroup merges (max, argmax) (wave shuffles +
-//     LDS, lowest index on ties) and sums the threads' partials, moved to the chunk max, in
-//     fp64. Unmasked rows exit at once and are never read.
-//  2. commit_decide: one workgroup per sequence. It merges each masked row's chunks in chunk
-//     order (fp64), giving the row's token and an estimate of Z whose relative error is
-//     below 1e-5 (per fp32 partial: 64 terms, each exp2 of a scaled difference to the
-//     running max, and at most 9 rescalings; about 7e-6 in the worst case). A
-//     threshold decision is taken on the estimate only outside a relative band of 1e-4; the
-//     fallback is taken on the estimate only when its winner leads every other position by
-//     more than 4e-4. Positions inside a band are recomputed by the same workgroup over the
-//     full row with fp64 exp and decided on those values (conf = 1/Z > gamma, in fp64 as in
-//     exact arithmetic), so every integer output is the exact-arithmetic decision except
-//     for margins below fp64 rounding. Called behind the fused LM head (no logits in
-//     memory), the same kernel decides on the chunk estimates alone, without the bands.
+// How: the work is one pass over the masked rows' logits, so it is HBM bound. One launch:
+// commit_reduce_kernel has one workgroup per (row, vocabulary chunk).
+//  * Reduce: each thread issues its eight 16-byte non-temporal loads at once and consumes
+//    them in element order with an online max, lowest argmax and sum of exp2((x - m) *
+//    log2 e) relative to its running max m (rescaled when m grows); the workgroup merges
+//    (max, argmax) (wave shuffles + LDS, lowest index on ties) and sums the threads'
+//    partials, moved to the chunk max, in fp64, and stores one record per chunk. Unmasked
+//    rows are never read: their chunk-0 workgroup writes the row's outputs and the rest exit.
+//  * Decide: after its record is stored (release), a workgroup counts its arrival on its
+//    sequence's counter (a 64-bit word: this call's nonzero 32-bit tag, then a count; a
+//    word carrying another tag counts as zero, so the workspace needs no clearing and stale
+//    words from earlier calls are ignored). The workgroup that brings the count to (masked
+//    rows of the sequence) x (chunks) decides the sequence (acquire, then the records) and
+//    resets the word, so a replay that reuses the tag (a captured graph) starts afresh.
+//    Deciding merges each masked row's chunks in chunk order (fp64), giving the row's token
+//    and an estimate of Z whose relative error is below 1e-5 (per fp32 partial: 64 terms,
+//    each exp2 of a scaled difference to the running max, and at most 9 rescalings; about
+//    7e-6 in the worst case). A threshold decision is taken on the estimate only outside a
+//    relative band of 1e-4; the fallback is taken on the estimate only when its winner leads
+//    every other position by more than 4e-4. Positions inside a band are recomputed by the
+//    same workgroup over the full row with fp64 exp and decided on those values (conf = 1/Z
+//    > gamma, in fp64 as in exact arithmetic), so every integer output is the
+//    exact-arithmetic decision except for margins below fp64 rounding.
+//  * Behind the fused LM head (no logits in memory) a separate launch,
+//    commit_decide_kernel, decides each sequence on the merged chunk estimates alone,
+//    without the bands.
 #include "tt_internal.h"
 
 namespace tt {
@@ -53,17 +60,241 @@ __device__ __forceinline__ void argmax_merge(float& m, int& tok, float m2, int t
   }
 }
 
+// ---- per-sequence decision (by one workgroup of NTH threads) ---------------------------
+
+template <int NTH>
+__device__ __forceinline__ double dblock_max(double v, double* red) {
+  for (int off = 32; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off, 64));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  double r = red[0];
+  for (int k = 1; k < NTH / 64; ++k) r = fmax(r, red[k]);
+  return r;
+}
+
+template <int NTH>
+__device__ __forceinline__ double dblock_sum(double v, double* red) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  double r = red[0];
+  for (int k = 1; k < NTH / 64; ++k) r += red[k];
+  return r;
+}
+
+template <int NTH>
+__device__ __forceinline__ int iblock_min(int v, int* red) {
+  for (int off = 32; off > 0; off >>= 1) v = min(v, __shfl_xor(v, off, 64));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int r = red[0];
+  for (int k = 1; k < NTH / 64; ++k) r = min(r, red[k]);
+  return r;
+}
+
+template <int NTH>
+__device__ __forceinline__ int iblock_sum(int v, int* red) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int r = red[0];
+  for (int k = 1; k < NTH / 64; ++k) r += red[k];
+  return r;
+}
+
+// fp64 Z of one row, by the whole workgroup (fixed reduction order: deterministic)
+template <typename T, int NTH>
+__device__ double row_z_fp64(const T* row, int V, double M, double* red) {
+  double z = 0.0;
+  for (int v = threadIdx.x; v < V; v += NTH) z += exp((double)to_f(row[v]) - M);
+  return dblock_sum<NTH>(z, red);
+}
+
+struct DecideSmem {
+  double redd[16];
+  int redi[16];
+  int nl;
+  float Mf;
+  int flagged[1024];
+};
+
+// Decide sequence b from its rows' chunk records: tokens, confidences, the gamma rule with
+// the fallback, and the fp64 recheck of the rows inside a band (when a.logits is given).
+// Writes the outputs of the masked rows, and of the unmasked rows too when write_unmasked.
+template <typename T, int NTH>
+__device__ void decide_sequence(const CommitArgs& a, int b, bool write_unmasked, DecideSmem& sh) {
+  constexpr int MAXP = 1024 / NTH;  // positions per thread (S <= 1024)
+  const int tid = threadIdx.x;
+  const T* logits = static_cast<const T*>(a.logits);
+  bool msk[MAXP];
+  float mm[MAXP];
+  double zz[MAXP];
+  int tk[MAXP], fl[MAXP], dec[MAXP];
+  int any_c = 0, nflag = 0, nmask = 0;
+  const bool exact = a.logits != nullptr;  // else: no logits to recompute from
+#pragma unroll
+  for (int p = 0; p < MAXP; ++p) {
+    const int i = tid + p * NTH;
+    const size_t row = (size_t)b * a.S + i;
+    msk[p] = i < a.S && a.mask[row];
+    mm[p] = -INFINITY;
+    zz[p] = 1.0;
+    tk[p] = -1;
+    fl[p] = dec[p] = 0;
+    if (write_unmasked && i < a.S && !msk[p]) {
+      a.token_id[row] = -1;
+      a.committed[row] = 0;
+      if (a.conf) a.conf[row] = 0.0f;
+    }
+    if (!msk[p]) continue;
+    ++nmask;
+    // merge the row's chunks in chunk order
+    const CommitChunk* c = a.chunks + row * a.n_chunks;
+    float M = -INFINITY;
+    int tok = 0x7fffffff;
+#pragma unroll 1
+    for (int k = 0; k < a.n_chunks; ++k) argmax_merge(M, tok, c[k].m, c[k].tok);
+    double Z = 0.0;
+#pragma unroll 1
+    for (int k = 0; k < a.n_chunks; ++k) Z += c[k].z * exp((double)c[k].m - (double)M);
+    mm[p] = M;
+    tk[p] = tok;
+    zz[p] = Z;
+    const double zg = Z * (double)a.gamma;
+    if (exact && fabs(zg - 1.0) <= kBand) {
+      fl[p] = 1;
+      ++nflag;
+    } else {
+      dec[p] = zg < 1.0;
+    }
+    any_c |= dec[p];
+  }
+  any_c = __syncthreads_or(any_c);
+  nmask = iblock_sum<NTH>(nmask, sh.redi);
+  int nflag_tot = iblock_sum<NTH>(nflag, sh.redi);
+  // fallback on the estimates when it is unambiguous; otherwise flag every candidate
+  bool fallback_pending = false;
+  if (!any_c && nmask > 0) {
+    double my = -1.0;
+#pragma unroll
+    for (int p = 0; p < MAXP; ++p)
+      if (msk[p]) my = fmax(my, 1.0 / zz[p]);
+    const double best = dblock_max<NTH>(my, sh.redd);
+    int mi = 0x7fffffff;
+#pragma unroll
+    for (int p = 0; p < MAXP; ++p)
+      if (msk[p] && 1.0 / zz[p] == best) mi = min(mi, tid + p * NTH);
+    const int bi = iblock_min<NTH>(mi, sh.redi);
+    double my2 = -1.0;
+#pragma unroll
+    for (int p = 0; p < MAXP; ++p)
+      if (msk[p] && tid + p * NTH != bi) my2 = fmax(my2, 1.0 / zz[p]);
+    const double second = dblock_max<NTH>(my2, sh.redd);
+    if (exact && (nflag_tot > 0 || (second >= 0.0 && best <= second * (1.0 + kFallBand)))) {
+      fallback_pending = true;
+#pragma unroll
+      for (int p = 0; p < MAXP; ++p)
+        if (msk[p] && fl[p] == 0 && (1.0 / zz[p]) * (1.0 + kFallBand) >= best) {
+          fl[p] = 1;
+          ++nflag;
+        }
+      nflag_tot = iblock_sum<NTH>(nflag, sh.redi);
+    } else {
+#pragma unroll
+      for (int p = 0; p < MAXP; ++p)
+        if (tid + p * NTH == bi) dec[p] = 1;
+    }
+  }
+  if (nflag_tot > 0) {
+    // fp64 recomputation of every flagged row by the whole workgroup
+    if (tid == 0) sh.nl = 0;
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < MAXP; ++p)
+      if (fl[p]) sh.flagged[atomicAdd(&sh.nl, 1)] = tid + p * NTH;
+    __syncthreads();
+    const int n = sh.nl;
+    for (int f = 0; f < n; ++f) {
+      const int i = sh.flagged[f];
+      const size_t row = (size_t)b * a.S + i;
+      if ((i % NTH) == tid) sh.Mf = mm[i / NTH];
+      __syncthreads();
+      const double z = row_z_fp64<T, NTH>(logits + row * a.V, a.V, (double)sh.Mf, sh.redd);
+      if ((i % NTH) == tid) zz[i / NTH] = z;
+      __syncthreads();
+    }
+    any_c = 0;
+#pragma unroll
+    for (int p = 0; p < MAXP; ++p) {
+      if (!msk[p]) continue;
+      if (fl[p]) dec[p] = (1.0 / zz[p]) > (double)a.gamma;  // band rows decided exactly
+      any_c |= dec[p];
+    }
+    any_c = __syncthreads_or(any_c);
+    if (!any_c && (fallback_pending || nmask > 0)) {
+      // most confident masked position (flagged rows carry exact values; every other row
+      // is outside the candidate band), lowest position on ties
+      double my = -1.0;
+#pragma unroll
+      for (int p = 0; p < MAXP; ++p)
+        if (msk[p]) my = fmax(my, 1.0 / zz[p]);
+      const double best = dblock_max<NTH>(my, sh.redd);
+      int mi = 0x7fffffff;
+#pragma unroll
+      for (int p = 0; p < MAXP; ++p)
+        if (msk[p] && 1.0 / zz[p] == best) mi = min(mi, tid + p * NTH);
+      const int bi = iblock_min<NTH>(mi, sh.redi);
+#pragma unroll
+      for (int p = 0; p < MAXP; ++p)
+        if (tid + p * NTH == bi) dec[p] = 1;
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < MAXP; ++p) {
+    if (!msk[p]) continue;
+    const size_t row = (size_t)b * a.S + tid + p * NTH;
+    a.token_id[row] = tk[p];
+    a.committed[row] = dec[p] ? 1 : 0;
+    if (a.conf) a.conf[row] = (float)(1.0 / zz[p]);
+  }
+}
+
+// ---- the commit: per-chunk reduction, then the sequence's last arrival decides -----------
+
 template <typename T>
 __global__ __launch_bounds__(NT) void commit_reduce_kernel(CommitArgs a) {
   constexpr int VE = Vec<T>::N;
   __shared__ float sm_m[4];
   __shared__ int sm_t[4];
   __shared__ double sm_z[4];
+  __shared__ int sm_n[4];
+  __shared__ int sm_last;
+  __shared__ DecideSmem dsm;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const long long blk = blockIdx.x;
-  const int row = (int)(blk / a.n_chunks);
-  const int ch = (int)(blk - (long long)row * a.n_chunks);
-  if (!a.mask[row]) return;
+  const int blk = blockIdx.x;
+  const int row = blk / a.n_chunks;
+  const int ch = blk - row * a.n_chunks;
+  if (!a.mask[row]) {
+    if (ch == 0 && tid == 0) {  // an unmasked row: its outputs, and nothing read
+      a.token_id[row] = -1;
+      a.committed[row] = 0;
+      if (a.conf) a.conf[row] = 0.0f;
+    }
+    return;
+  }
+  const int b = row / a.S;
+  // this thread's share of the sequence's mask (S <= 1024 = 4 per thread), loaded before
+  // the logits so that its wait does not hold them up
+  int nm = 0;
+#pragma unroll
+  for (int k = 0; k < 1024 / NT; ++k) {
+    const int i = tid + k * NT;
+    if (i < a.S) nm += a.mask[(size_t)b * a.S + i] != 0;
+  }
   const T* base = static_cast<const T*>(a.logits) + (size_t)row * a.V;
   const int begin = ch * a.chunk_elems;
   const int end = min(a.V, begin + a.chunk_elems);
@@ -120,10 +351,12 @@ __global__ __launch_bounds__(NT) void commit_reduce_kernel(CommitArgs a) {
     const float m2 = __shfl_xor(m, off, 64);
     const int t2 = __shfl_xor(tok, off, 64);
     argmax_merge(m, tok, m2, t2);
+    nm += __shfl_xor(nm, off, 64);
   }
   if (lane == 0) {
     sm_m[w] = m;
     sm_t[w] = tok;
+    sm_n[w] = nm;
   }
   __syncthreads();
   float M = sm_m[0];
@@ -142,228 +375,49 @@ __global__ __launch_bounds__(NT) void commit_reduce_kernel(CommitArgs a) {
     c.tok = TOK;
     c.z = (sm_z[0] + sm_z[1]) + (sm_z[2] + sm_z[3]);
     a.chunks[(size_t)row * a.n_chunks + ch] = c;
+    // release the record, then count this chunk's arrival on the sequence's word
+    __threadfence();
+    const uint32_t total = (uint32_t)((sm_n[0] + sm_n[1]) + (sm_n[2] + sm_n[3])) * (uint32_t)a.n_chunks;
+    unsigned long long* word = a.arrivals + b;
+    unsigned long long seen = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    unsigned long long want, prev;
+    do {
+      prev = seen;
+      const uint32_t cnt = ((uint32_t)(prev >> 32) == a.tag) ? (uint32_t)prev + 1u : 1u;
+      want = ((unsigned long long)a.tag << 32) | cnt;
+      seen = atomicCAS(word, prev, want);
+    } while (seen != prev);
+    const int last = (uint32_t)want == total;
+    if (last) __hip_atomic_store(word, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sm_last = last;
   }
-}
-
-// ---- per-sequence decision -----------------------------------------------------------
-
-constexpr int DT = 512;            // threads of the decision workgroup
-constexpr int DW = DT / 64;
-constexpr int MAXP = 1024 / DT;    // positions per thread (S <= 1024)
-
-__device__ __forceinline__ double dblock_max(double v, double* red) {
-  for (int off = 32; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off, 64));
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  double r = red[0];
-  for (int k = 1; k < DW; ++k) r = fmax(r, red[k]);
-  return r;
-}
-
-__device__ __forceinline__ double dblock_sum(double v, double* red) {
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  double r = red[0];
-  for (int k = 1; k < DW; ++k) r += red[k];
-  return r;
-}
-
-__device__ __forceinline__ int iblock_min(int v, int* red) {
-  for (int off = 32; off > 0; off >>= 1) v = min(v, __shfl_xor(v, off, 64));
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  int r = red[0];
-  for (int k = 1; k < DW; ++k) r = min(r, red[k]);
-  return r;
-}
-
-__device__ __forceinline__ int iblock_sum(int v, int* red) {
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  int r = red[0];
-  for (int k = 1; k < DW; ++k) r += red[k];
-  return r;
-}
-
-// fp64 Z of one row, by the whole workgroup (fixed reduction order: deterministic)
-template <typename T>
-__device__ double row_z_fp64(const T* row, int V, double M, double* red) {
-  double z = 0.0;
-  for (int v = threadIdx.x; v < V; v += DT) z += exp((double)to_f(row[v]) - M);
-  return dblock_sum(z, red);
+  if (!sm_last) return;
+  __threadfence();  // acquire: every record of the sequence is visible from here
+  decide_sequence<T, NT>(a, b, false, dsm);
 }
 
 template <typename T>
-__global__ __launch_bounds__(DT) void commit_decide_kernel(CommitArgs a) {
-  __shared__ double redd[DW];
-  __shared__ int redi[DW];
-  __shared__ int flagged_list[1024];
-  const int b = blockIdx.x, tid = threadIdx.x;
-  const T* logits = static_cast<const T*>(a.logits);
-  bool msk[MAXP];
-  float mm[MAXP];
-  double zz[MAXP];
-  int tk[MAXP], fl[MAXP], dec[MAXP];
-  int any_c = 0, nflag = 0, nmask = 0;
-  const bool exact = a.logits != nullptr;  // else: no logits to recompute from
-#pragma unroll
-  for (int p = 0; p < MAXP; ++p) {
-    const int i = tid + p * DT;
-    const size_t row = (size_t)b * a.S + i;
-    msk[p] = i < a.S && a.mask[row];
-    mm[p] = -INFINITY;
-    zz[p] = 1.0;
-    tk[p] = -1;
-    fl[p] = dec[p] = 0;
-    if (i < a.S && !msk[p]) {
-      a.token_id[row] = -1;
-      a.committed[row] = 0;
-      if (a.conf) a.conf[row] = 0.0f;
-    }
-    if (!msk[p]) continue;
-    ++nmask;
-    // merge the row's chunks in chunk order
-    const CommitChunk* c = a.chunks + row * a.n_chunks;
-    float M = -INFINITY;
-    int tok = 0x7fffffff;
-#pragma unroll 8
-    for (int k = 0; k < a.n_chunks; ++k) argmax_merge(M, tok, c[k].m, c[k].tok);
-    double Z = 0.0;
-#pragma unroll 8
-    for (int k = 0; k < a.n_chunks; ++k) Z += c[k].z * exp((double)c[k].m - (double)M);
-    mm[p] = M;
-    tk[p] = tok;
-    zz[p] = Z;
-    const double zg = Z * (double)a.gamma;
-    if (exact && fabs(zg - 1.0) <= kBand) {
-      fl[p] = 1;
-      ++nflag;
-    } else {
-      dec[p] = zg < 1.0;
-    }
-    any_c |= dec[p];
-  }
-  any_c = __syncthreads_or(any_c);
-  nmask = iblock_sum(nmask, redi);
-  int nflag_tot = iblock_sum(nflag, redi);
-  // fallback on the estimates when it is unambiguous; otherwise flag every candidate
-  bool fallback_pending = false;
-  if (!any_c && nmask > 0) {
-    double my = -1.0;
-#pragma unroll
-    for (int p = 0; p < MAXP; ++p)
-      if (msk[p]) my = fmax(my, 1.0 / zz[p]);
-    const double best = dblock_max(my, redd);
-    int mi = 0x7fffffff;
-#pragma unroll
-    for (int p = 0; p < MAXP; ++p)
-      if (msk[p] && 1.0 / zz[p] == best) mi = min(mi, tid + p * DT);
-    const int bi = iblock_min(mi, redi);
-    double my2 = -1.0;
-#pragma unroll
-    for (int p = 0; p < MAXP; ++p)
-      if (msk[p] && tid + p * DT != bi) my2 = fmax(my2, 1.0 / zz[p]);
-    const double second = dblock_max(my2, redd);
-    if (exact && (nflag_tot > 0 || (second >= 0.0 && best <= second * (1.0 + kFallBand)))) {
-      fallback_pending = true;
-#pragma unroll
-      for (int p = 0; p < MAXP; ++p)
-        if (msk[p] && fl[p] == 0 && (1.0 / zz[p]) * (1.0 + kFallBand) >= best) {
-          fl[p] = 1;
-          ++nflag;
-        }
-      nflag_tot = iblock_sum(nflag, redi);
-    } else {
-#pragma unroll
-      for (int p = 0; p < MAXP; ++p)
-        if (tid + p * DT == bi) dec[p] = 1;
-    }
-  }
-  if (nflag_tot > 0) {
-    // fp64 recomputation of every flagged row by the whole workgroup
-    __shared__ int nl;
-    if (tid == 0) nl = 0;
-    __syncthreads();
-#pragma unroll
-    for (int p = 0; p < MAXP; ++p)
-      if (fl[p]) flagged_list[atomicAdd(&nl, 1)] = tid + p * DT;
-    __syncthreads();
-    const int n = nl;
-    for (int f = 0; f < n; ++f) {
-      const int i = flagged_list[f];
-      const size_t row = (size_t)b * a.S + i;
-      __shared__ float Mf;
-      if ((i % DT) == tid) Mf = mm[i / DT];
-      __syncthreads();
-      const double z = row_z_fp64(logits + row * a.V, a.V, (double)Mf, redd);
-      if ((i % DT) == tid) zz[i / DT] = z;
-      __syncthreads();
-    }
-    any_c = 0;
-#pragma unroll
-    for (int p = 0; p < MAXP; ++p) {
-      if (!msk[p]) continue;
-      if (fl[p]) dec[p] = (1.0 / zz[p]) > (double)a.gamma;  // band rows decided exactly
-      any_c |= dec[p];
-    }
-    any_c = __syncthreads_or(any_c);
-    if (!any_c && (fallback_pending || nmask > 0)) {
-      // most confident masked position (flagged rows carry exact values; every other row
-      // is outside the candidate band), lowest position on ties
-      double my = -1.0;
-#pragma unroll
-      for (int p = 0; p < MAXP; ++p)
-        if (msk[p]) my = fmax(my, 1.0 / zz[p]);
-      const double best = dblock_max(my, redd);
-      int mi = 0x7fffffff;
-#pragma unroll
-      for (int p = 0; p < MAXP; ++p)
-        if (msk[p] && 1.0 / zz[p] == best) mi = min(mi, tid + p * DT);
-      const int bi = iblock_min(mi, redi);
-#pragma unroll
-      for (int p = 0; p < MAXP; ++p)
-        if (tid + p * DT == bi) dec[p] = 1;
-    }
-  }
-#pragma unroll
-  for (int p = 0; p < MAXP; ++p) {
-    if (!msk[p]) continue;
-    const size_t row = (size_t)b * a.S + tid + p * DT;
-    a.token_id[row] = tk[p];
-    a.committed[row] = dec[p] ? 1 : 0;
-    if (a.conf) a.conf[row] = (float)(1.0 / zz[p]);
-  }
+__global__ __launch_bounds__(512) void commit_decide_kernel(CommitArgs a) {
+  __shared__ DecideSmem dsm;
+  decide_sequence<T, 512>(a, blockIdx.x, true, dsm);
 }
 
 }  // namespace
 
 hipError_t launch_commit_decide(const CommitArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(commit_decide_kernel<uint16_t>, dim3(a.B), dim3(DT), 0, s, a);
+  hipLaunchKernelGGL(commit_decide_kernel<uint16_t>, dim3(a.B), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
 int commit_chunk_elems(int dtype) { return NT * LOADS * (dtype == TT_BF16 ? 8 : 4); }
 
-hipError_t launch_commit(const CommitArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+hipError_t launch_commit(const CommitArgs& a, hipStream_t s) {
   const long long nblk = (long long)a.B * a.S * a.n_chunks;
-  if (ev0) (void)hipEventRecord(ev0, s);
   if (a.dtype == TT_BF16)
     hipLaunchKernelGGL(commit_reduce_kernel<uint16_t>, dim3((unsigned)nblk), dim3(NT), 0, s, a);
   else
     hipLaunchKernelGGL(commit_reduce_kernel<float>, dim3((unsigned)nblk), dim3(NT), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (ev1) (void)hipEventRecord(ev1, s);
-  if (a.dtype == TT_BF16)
-    hipLaunchKernelGGL(commit_decide_kernel<uint16_t>, dim3(a.B), dim3(DT), 0, s, a);
-  else
-    hipLaunchKernelGGL(commit_decide_kernel<float>, dim3(a.B), dim3(DT), 0, s, a);
   return hipGetLastError();
 }
 

@@ -1,6 +1,9 @@
 // libtt C-ABI: argument validation, workspace layout, launches and kernel timing.
 // The operations themselves are documented in include/tt.h.
 #include <math.h>
+
+#include <atomic>
+#include <chrono>
 #include <mutex>
 #include <vector>
 
@@ -54,19 +57,35 @@ tt_status plan_attn(const tt_attn_shape* sh, AttnPlan* p) {
 
 struct CommitPlan {
   int n_chunks, chunk_elems;
-  size_t chunk_bytes;
+  size_t chunk_bytes, arrival_bytes;
 };
 
 tt_status plan_commit(int32_t B, int32_t S, int32_t V, int32_t dtype, CommitPlan* p) {
   if (B < 0 || S < 1 || V < 1) return TT_ERR_INVALID_ARG;
   if (dtype != TT_F32 && dtype != TT_BF16) return TT_ERR_UNSUPPORTED;
   if (S > 1024) return TT_ERR_UNSUPPORTED;
-  if ((long long)B * S * V >= (1LL << 40)) return TT_ERR_UNSUPPORTED;
   p->chunk_elems = commit_chunk_elems(dtype);
   p->n_chunks = (V + p->chunk_elems - 1) / p->chunk_elems;
+  // one workgroup per (row, chunk): the launch grid bounds the shape
+  if ((long long)B * S * p->n_chunks > kMaxGridBlocks) return TT_ERR_UNSUPPORTED;
   p->chunk_bytes = align_up((size_t)B * S * p->n_chunks * sizeof(CommitChunk));
-
+  p->arrival_bytes = align_up((size_t)B * sizeof(unsigned long long));
   return TT_OK;
+}
+
+// A nonzero 32-bit tag per commit call: a per-process salt (clock at first use) stepped by
+// a call counter through a 64-bit mixing function. Arrival words left by earlier calls, or
+// any other stale workspace contents, carry another tag and count as zero.
+uint32_t next_commit_tag() {
+  static const uint64_t salt =
+      (uint64_t)std::chrono::high_resolution_clock::now().time_since_epoch().count();
+  static std::atomic<uint64_t> calls{0};
+  uint64_t x = salt + 0x9E3779B97F4A7C15ull * (calls.fetch_add(1) + 1);
+  x = (x ^ (x >> 30)) * 0xBF58476D1CE4E5B9ull;
+  x = (x ^ (x >> 27)) * 0x94D049BB133111EBull;
+  x ^= x >> 31;
+  const uint32_t t = (uint32_t)x ^ (uint32_t)(x >> 32);
+  return t ? t : 1u;
 }
 
 struct LmPlan {
@@ -93,7 +112,7 @@ struct Profiler {
   std::mutex mu;
   bool enabled = false;
   std::vector<hipEvent_t> attn_ev[4];   // attn start, main start, main end, attn end
-  std::vector<hipEvent_t> commit_ev[3]; // commit start, reduce end, commit end
+  std::vector<hipEvent_t> commit_ev[2]; // commit start, commit end (one kernel)
   std::vector<hipEvent_t> lm_ev[3];     // LM-head commit start, reduce end, end
   int64_t attn_calls = 0, commit_calls = 0, lm_calls = 0;
   int attn_used = 0, commit_used = 0, lm_used = 0;
@@ -116,7 +135,12 @@ using namespace tt;
 
 extern "C" {
 
-int32_t tt_version(void) { return (1 << 16) | 0; }
+int32_t tt_version(void) { return (1 << 16) | 1; }
+
+#ifndef TT_SOURCE_HASH
+#error "TT_SOURCE_HASH must be defined by the build (block_diffusion_lm_tt_amd/build.py)"
+#endif
+const char* tt_build_id(void) { return TT_SOURCE_HASH; }
 
 const char* tt_status_str(tt_status s) {
   switch (s) {
@@ -148,6 +172,10 @@ tt_status tt_block_denoise_attn(const tt_attn_shape* shape, const void* q, const
   if (shape->Lmax > 0 && (!k_ctx || !v_ctx)) return TT_ERR_INVALID_ARG;
   const size_t need = tt_block_denoise_attn_workspace(shape);
   if (!workspace || workspace_bytes < need) return TT_ERR_WORKSPACE;
+  // the MFMA path copies 16-byte pieces: a base off that boundary takes the element-wise path
+  const uintptr_t bases = (uintptr_t)q | (uintptr_t)k_blk | (uintptr_t)v_blk | (uintptr_t)k_ctx |
+                          (uintptr_t)v_ctx | (uintptr_t)o;
+  const bool mfma = p.mfma && bases % 16 == 0;
 
   AttnArgs a;
   a.q = q;
@@ -184,7 +212,7 @@ tt_status tt_block_denoise_attn(const tt_attn_shape* shape, const void* q, const
   }
   if (ev[0]) (void)hipEventRecord(ev[0], stream);
   hipError_t e;
-  if (p.mfma) {
+  if (mfma) {
     e = launch_attn_mfma(a, stream, ev[1], ev[2]);
   } else {
     if (ev[1]) (void)hipEventRecord(ev[1], stream);
@@ -198,7 +226,7 @@ tt_status tt_block_denoise_attn(const tt_attn_shape* shape, const void* q, const
 size_t tt_commit_workspace(int32_t B, int32_t S, int32_t V, int32_t dtype) {
   CommitPlan p;
   if (plan_commit(B, S, V, dtype, &p) != TT_OK) return 0;
-  const size_t n = p.chunk_bytes;
+  const size_t n = p.chunk_bytes + p.arrival_bytes;
   return n < kAlign ? kAlign : n;
 }
 
@@ -223,6 +251,8 @@ tt_status tt_commit(int32_t B, int32_t S, int32_t V, int32_t dtype, const void* 
   a.conf = conf;
   char* ws = static_cast<char*>(workspace);
   a.chunks = reinterpret_cast<CommitChunk*>(ws);
+  a.arrivals = reinterpret_cast<unsigned long long*>(ws + p.chunk_bytes);
+  a.tag = next_commit_tag();
   a.B = B;
   a.S = S;
   a.V = V;
@@ -230,20 +260,21 @@ tt_status tt_commit(int32_t B, int32_t S, int32_t V, int32_t dtype, const void* 
   a.chunk_elems = p.chunk_elems;
   a.dtype = dtype;
 
-  hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+  hipEvent_t ev[2] = {nullptr, nullptr};
   {
     std::lock_guard<std::mutex> lk(g_prof.mu);
     if (g_prof.enabled) {
       ++g_prof.commit_calls;
       if (g_prof.commit_used < kMaxTimed) {
-        for (int k = 0; k < 3; ++k) ev[k] = ev_slot(g_prof.commit_ev[k], g_prof.commit_used);
-        if (ev[0] && ev[1] && ev[2]) ++g_prof.commit_used;
-        else ev[0] = ev[1] = ev[2] = nullptr;
+        for (int k = 0; k < 2; ++k) ev[k] = ev_slot(g_prof.commit_ev[k], g_prof.commit_used);
+        if (ev[0] && ev[1]) ++g_prof.commit_used;
+        else ev[0] = ev[1] = nullptr;
       }
     }
   }
-  hipError_t e = launch_commit(a, stream, ev[0], ev[1]);
-  if (ev[2]) (void)hipEventRecord(ev[2], stream);
+  if (ev[0]) (void)hipEventRecord(ev[0], stream);
+  hipError_t e = launch_commit(a, stream);
+  if (ev[1]) (void)hipEventRecord(ev[1], stream);
   return e == hipSuccess ? TT_OK : TT_ERR_HIP;
 }
 
@@ -263,6 +294,7 @@ tt_status tt_lmhead_commit(int32_t B, int32_t S, int32_t K, int32_t V, const voi
   if (isnan(gamma)) return TT_ERR_INVALID_ARG;
   if (B == 0) return TT_OK;
   if (!hidden || !weight || !mask || !token_id || !committed) return TT_ERR_INVALID_ARG;
+  if (((uintptr_t)hidden | (uintptr_t)weight) % 16 != 0) return TT_ERR_UNSUPPORTED;  // 16-byte loads
   const size_t need = tt_lmhead_commit_workspace(B, S, K, V);
   if (!workspace || workspace_bytes < need) return TT_ERR_WORKSPACE;
 
@@ -287,6 +319,8 @@ tt_status tt_lmhead_commit(int32_t B, int32_t S, int32_t K, int32_t V, const voi
   c.committed = committed;
   c.conf = conf;
   c.chunks = l.merged;
+  c.arrivals = nullptr;  // the separate decide launch counts no arrivals
+  c.tag = 0;
   c.B = B;
   c.S = S;
   c.V = V;
@@ -373,11 +407,10 @@ tt_status tt_profile_read(tt_profile_stats* out) {
     s.attn_main_ms += ms;
   }
   for (int k = 0; k < g_prof.commit_used; ++k) {
-    if (hipEventSynchronize(g_prof.commit_ev[2][k]) != hipSuccess) return TT_ERR_HIP;
-    if (hipEventElapsedTime(&ms, g_prof.commit_ev[0][k], g_prof.commit_ev[2][k]) != hipSuccess) return TT_ERR_HIP;
-    s.commit_total_ms += ms;
+    if (hipEventSynchronize(g_prof.commit_ev[1][k]) != hipSuccess) return TT_ERR_HIP;
     if (hipEventElapsedTime(&ms, g_prof.commit_ev[0][k], g_prof.commit_ev[1][k]) != hipSuccess) return TT_ERR_HIP;
-    s.commit_reduce_ms += ms;
+    s.commit_total_ms += ms;
+    s.commit_reduce_ms += ms;  // the reduction and the decisions are one kernel
   }
   for (int k = 0; k < g_prof.lm_used; ++k) {
     if (hipEventSynchronize(g_prof.lm_ev[2][k]) != hipSuccess) return TT_ERR_HIP;

@@ -85,6 +85,8 @@ class AttnInputs:
     k_ctx: np.ndarray
     v_ctx: np.ndarray
     ctx_len: np.ndarray  # int32 [B]
+    # planted hot keys (make_attn with hot_keys): {(b, g): context positions}, else None
+    hot: Optional[dict] = None
 
     @property
     def ctx_kv_bytes(self) -> int:
@@ -180,6 +182,7 @@ def make_attn(B: int, S: int, Hq: int, Hkv: int, D: int, ctx_lens: Sequence[int]
         n = int(ctx[b])
         kc[b, :n] = _normal(rk, (n, Hkv, D))
         vc[b, :n] = _normal(rv, (n, Hkv, D))
+    hot_sets = {} if hot_keys else None
     if hot_keys:
         G = Hq // Hkv
         kappa = math.sqrt(float(hot_keys.get("boost", 8.0)) * math.sqrt(D))
@@ -194,6 +197,7 @@ def make_attn(B: int, S: int, Hq: int, Hkv: int, D: int, ctx_lens: Sequence[int]
                 if nh:
                     hot = rb.choice(n, size=nh, replace=False)
                     kc[b, hot, g] += np.float32(kappa) * u
+                    hot_sets[(b, g)] = np.sort(hot)
             q[:, :, g * G:(g + 1) * G] += np.float32(kappa) * u
     # padding rows
     if dtype == BF16:
@@ -207,7 +211,7 @@ def make_attn(B: int, S: int, Hq: int, Hkv: int, D: int, ctx_lens: Sequence[int]
         kc_e[b, n:] = fillv
         vc_e[b, n:] = fillv
     return AttnInputs(B, S, Hq, Hkv, D, Lmax, dtype, _encode(q, dtype), _encode(kb, dtype),
-                      _encode(vb, dtype), kc_e, vc_e, ctx)
+                      _encode(vb, dtype), kc_e, vc_e, ctx, hot_sets)
 
 
 def make_block_qkv(B: int, S: int, Hq: int, Hkv: int, D: int, dtype: str = BF16, seed: int = 0,

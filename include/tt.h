@@ -56,6 +56,11 @@ typedef struct {
 /* Library version, (major << 16) | minor. */
 int32_t tt_version(void);
 
+/* Build identity: the first 16 hex digits of the SHA-256 of the sources this library was
+ * compiled from (static string, never NULL). A binding compares it with the sources beside
+ * it and refuses a stale library. */
+const char *tt_build_id(void);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char *tt_status_str(tt_status s);
 
@@ -85,9 +90,11 @@ const char *tt_status_str(tt_status s);
  * ctx_len lives on the device, so the host cannot check it; the kernels clamp each value
  * into [0, Lmax] before use (a value outside that range is a caller error, not a fault).
  *
- * Supported: dtype TT_BF16 or TT_F32; 1 <= D <= 256 (D == 128 with bf16 takes the MFMA
- * path); 1 <= S <= 1024; B*S*Hq*D, B*Lmax*Hkv*D < 2^31; B <= 8191. Anything else returns
- * TT_ERR_UNSUPPORTED. B == 0 is a no-op. k_ctx/v_ctx may be NULL only when Lmax == 0.
+ * Supported: dtype TT_BF16 or TT_F32; 1 <= D <= 256; 1 <= S <= 1024; B*S*Hq*D,
+ * B*Lmax*Hkv*D < 2^31; B <= 8191. Anything else returns TT_ERR_UNSUPPORTED. B == 0 is a
+ * no-op. k_ctx/v_ctx may be NULL only when Lmax == 0. Tensors need only their element
+ * alignment: bf16 with D == 128 takes the MFMA path when q, k_blk, v_blk, k_ctx, v_ctx and
+ * o all start on a 16-byte boundary (16-byte copies), and the element-wise path otherwise.
  * ------------------------------------------------------------------------------------- */
 size_t tt_block_denoise_attn_workspace(const tt_attn_shape *shape);
 
@@ -121,8 +128,15 @@ tt_status tt_block_denoise_attn(const tt_attn_shape *shape, const void *q, const
  *   committed  [B, S]      uint8                   (device, written)
  *   conf       [B, S]      float, may be NULL      (device, written)
  *
- * Supported: dtype TT_BF16 or TT_F32, 1 <= S <= 1024, 1 <= V, B*S*V < 2^40. B == 0 is a
- * no-op.
+ *   workspace  device memory of tt_commit_workspace(B, S, V, dtype) bytes: 16 bytes per
+ *              (position, vocabulary chunk of 16384 bf16 / 8192 fp32 entries) and 8 per
+ *              sequence (an arrival word tagged per call). Its contents on entry are
+ *              ignored: words left by other calls or other users carry another tag (a
+ *              stale word equals this call's 32-bit tag with probability 2^-32).
+ *
+ * Supported: dtype TT_BF16 or TT_F32, 1 <= S <= 1024, 1 <= V, and B*S*ceil(V/chunk) <=
+ * 16777215 (one workgroup per position and chunk); anything else returns
+ * TT_ERR_UNSUPPORTED. B == 0 is a no-op.
  * ------------------------------------------------------------------------------------- */
 size_t tt_commit_workspace(int32_t B, int32_t S, int32_t V, int32_t dtype);
 
@@ -161,7 +175,8 @@ tt_status tt_commit(int32_t B, int32_t S, int32_t V, int32_t dtype, const void *
  *              entry are ignored
  *
  * Supported: K a multiple of 64 (at most 2^20); 1 <= S <= 1024; B*S <= 4096;
- * B*S*K < 2^31; any V >= 1. Anything else returns TT_ERR_UNSUPPORTED. B == 0 is a no-op.
+ * B*S*K < 2^31; any V >= 1; hidden and weight starting on a 16-byte boundary (16-byte
+ * loads). Anything else returns TT_ERR_UNSUPPORTED. B == 0 is a no-op.
  * ------------------------------------------------------------------------------------- */
 size_t tt_lmhead_commit_workspace(int32_t B, int32_t S, int32_t K, int32_t V);
 
@@ -213,7 +228,8 @@ typedef struct {
     double attn_main_ms;      /* sum over those calls, the main attention kernel alone   */
     int64_t commit_calls;     /* tt_commit calls timed                                   */
     double commit_total_ms;   /* sum over those calls, first launch to last              */
-    double commit_reduce_ms;  /* sum over those calls, the vocabulary reduction kernel   */
+    double commit_reduce_ms;  /* sum over those calls, the commit's kernel (one launch:   */
+                              /* the vocabulary reduction, then the decisions)           */
     int64_t lm_calls;         /* tt_lmhead_commit calls timed                            */
     double lm_total_ms;       /* sum over those calls, first launch to last              */
     double lm_reduce_ms;      /* sum over those calls, the fused head + reduction kernel */

@@ -19,6 +19,23 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, n), f"libtt.so does not export {n}"
 
 
+def test_build_id_matches_the_sources_beside_it():
+    from block_diffusion_lm_tt_amd.build import source_hash
+    L = tt.lib()
+    bid = L.tt_build_id().decode()
+    assert len(bid) == 16 and bid == source_hash()
+
+
+def test_stale_library_is_refused(tmp_path, monkeypatch):
+    # a library whose build id differs from the sources' hash is never loaded
+    from block_diffusion_lm_tt_amd import build as B
+    monkeypatch.setattr(B, "source_hash", lambda: "0" * 16)
+    monkeypatch.setattr(_lib, "_LIB", None)
+    with pytest.raises(ImportError, match="other sources"):
+        _lib.lib()
+    monkeypatch.setattr(_lib, "_LIB", None)
+
+
 def test_version_and_status_strings():
     L = tt.lib()
     assert L.tt_version() >> 16 == 1
@@ -97,6 +114,12 @@ def test_commit_validation():
     assert call(args(B=-2)) == INVALID
     assert call(args(dt=3)) == UNSUPPORTED
     assert call(args(S=1025)) == UNSUPPORTED
+    # one workgroup per (position, 16384-entry chunk): the grid bounds B*S*chunks by 2^24 - 1
+    assert L.tt_commit_workspace(8191, 1024, 16384 * 3, 1) == 0
+    assert call(args(B=8191, S=1024, V=16384 * 3)) == UNSUPPORTED
+    assert L.tt_commit_workspace(1023, 1024, 16384 * 16, 1) > 0   # 16760832 workgroups fit
+    assert L.tt_commit_workspace(1024, 1024, 16384 * 16, 1) == 0  # 2^24 do not
+
     for k in ("lg", "mk", "tok", "com"):
         assert call(args(**{k: None})) == INVALID
     assert call(args(n=need - 1)) == WORKSPACE
@@ -122,6 +145,9 @@ def test_lmhead_commit_validation():
         assert call(args(**kw)) == UNSUPPORTED
     for k in ("h", "w", "mk", "tok", "com"):
         assert call(args(**{k: None})) == INVALID
+    # 16-byte loads of the hidden states and the head's rows
+    assert call(args(h=FAKE + 2)) == UNSUPPORTED
+    assert call(args(w=FAKE + 8)) == UNSUPPORTED
     assert call(args(n=need - 1)) == WORKSPACE
     assert call(args(ws=None)) == WORKSPACE
     assert call(args(B=0, h=None, w=None)) == 0

@@ -229,3 +229,16 @@ def test_lmhead_full_size_sampled(dev):
     seqs = [0, w3.B - 1]
     y = _sub(x, seqs)
     _check(y, (tok[seqs], com[seqs], conf[seqs]), _exact(y, x.gamma), x.gamma, "full size")
+
+
+def test_misaligned_operands_are_refused(dev):
+    # the kernel's 16-byte loads need 16-byte aligned hidden states and head rows: an
+    # operand off that boundary is refused (TT_ERR_UNSUPPORTED), nothing is launched
+    import block_diffusion_lm_tt_amd as tt
+    x = W.make_lmhead(1, 16, 64, 100, seed=8)
+    h, w, m = TZ.lmhead_to_device(x, dev)
+    buf = torch.empty(h.numel() + 1, dtype=h.dtype, device=dev)
+    h2 = buf[1:].view(h.shape)
+    h2.copy_(h)
+    with pytest.raises(tt.TTError, match="UNSUPPORTED"):
+        tt.tt_lmhead_commit(h2, w, m, 0.5)

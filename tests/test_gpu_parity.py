@@ -120,35 +120,45 @@ def test_attn_block_permutation_equivariance(dev):
     assert np.abs(b - a[:, perm]).max() <= 1e-2
 
 
+def _offset_copy(t, dev, off=1):
+    """t on the device starting `off` elements past a 16-byte boundary (contiguous)."""
+    buf = torch.empty(t.numel() + off, dtype=t.dtype, device=dev)
+    v = buf[off:off + t.numel()].view(t.shape)
+    v.copy_(t)
+    return v
+
+
+def test_attn_misaligned_inputs_take_the_elementwise_path(dev):
+    # bases off a 16-byte boundary cannot take the MFMA path's 16-byte copies: the library
+    # sends them to the element-wise kernel, with the same results
+    import block_diffusion_lm_tt_amd as tt
+    x = W.make_attn(2, 16, 32, 2, 128, [77, 300], Lmax=300, dtype=W.BF16, seed=21)
+    _say("attn misaligned bf16 D=128")
+    q, kb, vb, kc, vc, cl = TZ.attn_to_device(x, dev)
+    q2, kc2 = _offset_copy(q, dev), _offset_copy(kc, dev)
+    out = _offset_copy(torch.zeros_like(q), dev)
+    assert q2.data_ptr() % 16 and kc2.data_ptr() % 16 and out.data_ptr() % 16
+    tt.tt_block_denoise_attn(q2, kb, vb, kc2, vc, cl, out=out)
+    torch.cuda.synchronize()
+    _assert_attn(out.double().cpu().numpy(), _oracle_attn(x), W.BF16, "misaligned")
+
+
 def test_attn_deterministic_replay(dev):
     x = W.WORKLOADS[3].attn(B=8)
     assert np.array_equal(_gpu_attn(x, dev), _gpu_attn(x, dev))
 
 
 # ------------------------------------------------------------------------------------------------
-# attention at the workloads' full sizes: sampled sequences checked against the oracle
+# attention at the workloads' full sizes, every unit against the oracle (the block-loop
+# workload's calls are checked inside its loop: test_gpu_blockloop.py)
 # ------------------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
-def test_attn_workload_sampled(dev, cid):
+@pytest.mark.parametrize("cid", [1, 2, 3, 4])
+def test_attn_workload_full(dev, cid):
     w = W.WORKLOADS[cid]
     _say(f"attn workload {cid}: {w.name}")
-    x = w.attn(step=1 if cid == 5 else 0, layer=2 if cid == 5 else 0)
-    got = _gpu_attn(x, dev)
-    if cid in (1, 2):
-        _assert_attn(got, _oracle_attn(x), x.dtype, f"workload {cid}")
-        return
-    if cid == 3:  # shortest, longest and two more sequences, all heads
-        order = np.argsort(x.ctx_len)
-        picks = sorted({int(order[0]), int(order[-1]), 5, 17})
-        for b in picks:
-            _assert_attn(got[b:b + 1], _oracle_attn(_slice_b(x, b)), x.dtype, f"workload 3 b={b}")
-        return
-    G = x.Hq // x.Hkv
-    picks = [(0, 0), (x.B - 1, x.Hkv - 1)]
-    for b, g in picks:
-        want = _oracle_attn(_slice_b(x, b, heads=(g, G)))
-        _assert_attn(got[b:b + 1, :, g * G:(g + 1) * G], want, x.dtype, f"workload {cid} b={b} g={g}")
+    x = w.attn()
+    _assert_attn(_gpu_attn(x, dev), _oracle_attn(x), x.dtype, f"workload {cid}, every unit")
 
 
 @pytest.mark.parametrize("dtype,D", [(W.BF16, 128), (W.F32, 64)])
@@ -164,25 +174,6 @@ def test_attn_ctx_len_outside_the_storage_is_clamped(dev, dtype, D):
     got = tt.tt_block_denoise_attn(q, kb, vb, kc, vc, wild)
     torch.cuda.synchronize()
     _assert_attn(got.double().cpu().numpy(), _oracle_attn(x), dtype, "clamped ctx_len")
-
-
-def test_attn_block_loop_every_layer_and_later_steps(dev):
-    # the block-loop workload as the loop runs it: each layer's own context KV with the block
-    # Q/K/V of (step, layer); all 6 layers at step 0 and a seeded sample of later (step, layer)
-    import dataclasses
-    w = W.WORKLOADS[5]
-    rng = np.random.default_rng(w.seed)
-    later = list(zip(rng.integers(1, w.steps, 3).tolist(), rng.integers(0, w.layers, 3).tolist()))
-    G = w.Hq // w.Hkv
-    for t, l in [(0, l) for l in range(w.layers)] + later:
-        _say(f"attn block loop step {t} layer {l}")
-        x = w.attn(step=0, layer=l)
-        q, kb, vb = w.block_qkv(t, l)
-        x = dataclasses.replace(x, q=q, k_blk=kb, v_blk=vb)
-        got = _gpu_attn(x, dev)
-        b, g = (7 * t + 3 * l) % w.B, (t + l) % w.Hkv
-        want = _oracle_attn(_slice_b(x, b, heads=(g, G)))
-        _assert_attn(got[b:b + 1, :, g * G:(g + 1) * G], want, x.dtype, f"block loop t={t} l={l} b={b} g={g}")
 
 
 # ------------------------------------------------------------------------------------------------
@@ -203,7 +194,8 @@ def _oracle_commit(c: W.CommitInputs, gamma=None):
 
 
 def _assert_commit(c, dev, gamma=None, what=""):
-    g = c.gamma if gamma is None else gamma
+    # the threshold as the C-ABI receives it (a C float) goes to both sides: one rule
+    g = float(np.float32(c.gamma if gamma is None else gamma))
     tok, com, conf = _gpu_commit(c, dev, g)
     otok, ocom, oconf, oz = _oracle_commit(c, g)
     assert np.array_equal(tok, otok), f"{what}: token_id differs at {np.argwhere(tok != otok)[:5]}"
