@@ -6,32 +6,30 @@
 // Z = sum_v exp(l_v - max), conf = 1/Z, committed = conf > gamma; a sequence with masked
 // positions and no commit commits its most confident masked position (lowest i on ties).
 //
-// How: the work is one pass over the masked rows' logits, so it is HBM bound. One launch:
-// commit_reduce_kernel has one workgroup per (row, vocabulary chunk).
-//  * Reduce: each thread issues its eight 16-byte non-temporal loads at once and consumes
-//    them in element order with an online max, lowest argmax and sum of exp2((x - m) *
-//    log2 e) relative to its running max m (rescaled when m grows); the workgroup merges
-//    (max, argmax) (wave shuffles + LDS, lowest index on ties) and sums the threads'
-//    partials, moved to the chunk max, in fp64, and stores one record per chunk. Unmasked
-//    rows are never read: their chunk-0 workgroup writes the row's outputs and the rest exit.
-//  * Decide: after its record is stored (release), a workgroup counts its arrival on its
-//    sequence's counter (a 64-bit word: this call's nonzero 32-bit tag, then a count; a
-//    word carrying another tag counts as zero, so the workspace needs no clearing and stale
-//    words from earlier calls are ignored). The workgroup that brings the count to (masked
-//    rows of the sequence) x (chunks) decides the sequence (acquire, then the records) and
-//    resets the word, so a replay that reuses the tag (a captured graph) starts afresh.
-//    Deciding merges each masked row's chunks in chunk order (fp64), giving the row's token
-//    and an estimate of Z whose relative error is below 1e-5 (per fp32 partial: 64 terms,
-//    each exp2 of a scaled difference to the running max, and at most 9 rescalings; about
-//    7e-6 in the worst case). A threshold decision is taken on the estimate only outside a
-//    relative band of 1e-4; the fallback is taken on the estimate only when its winner leads
-//    every other position by more than 4e-4. Positions inside a band are recomputed by the
-//    same workgroup over the full row with fp64 exp and decided on those values (conf = 1/Z
-//    > gamma, in fp64 as in exact arithmetic), so every integer output is the
-//    exact-arithmetic decision except for margins below fp64 rounding.
-//  * Behind the fused LM head (no logits in memory) a separate launch,
-//    commit_decide_kernel, decides each sequence on the merged chunk estimates alone,
-//    without the bands.
+// How: the work is one pass over the masked rows' logits, so it is HBM bound. Two launches,
+// with no communication between workgroups inside a launch:
+//  1. commit_reduce: one workgroup per (masked row, vocabulary chunk). Each thread issues its
+//     eight 16-byte non-temporal loads at once and consumes them in element order with an
+//     online max, lowest argmax and sum of exp2((x - m) * log2 e) relative to its running
+//     max m (rescaled when m grows); the workgroup merges (max, argmax) (wave shuffles +
+//     LDS, lowest index on ties) and sums the threads' partials, moved to the chunk max, in
+//     fp64. Unmasked rows exit at once and are never read.
+//  2. commit_decide: one workgroup per sequence. It merges each masked row's chunks in chunk
+//     order in one pass (all of a row's record loads in flight, online max / lowest argmax /
+//     fp64 sum rescaled by fp32 factors), giving the row's token and an estimate of Z whose
+//     relative error is below 1e-5 (per fp32 partial: 64 terms, each exp2 of a scaled
+//     difference to the running max, and at most 9 rescalings; about 7e-6 in the worst
+//     case). A threshold decision is taken on the estimate only outside a relative band of
+//     1e-4; the fallback is taken on the estimate only when its winner leads every other
+//     position by more than 4e-4. Positions inside a band are recomputed by the same
+//     workgroup over the full row with fp64 exp and decided on those values (conf = 1/Z >
+//     gamma, in fp64 as in exact arithmetic), so every integer output is the
+//     exact-arithmetic decision except for margins below fp64 rounding. Called behind the
+//     fused LM head (no logits in memory), the same kernel decides on the chunk estimates
+//     alone, without the bands.
+//  Folding step 2 into step 1 (the last-arriving workgroup of a sequence deciding) was built
+//  and measured slower: the arrival counters are device-scope atomics on one word per
+//  sequence, about 80 per word here, and they serialize (49.6 us per call against 25).
 #include "tt_internal.h"
 
 namespace tt {
@@ -152,15 +150,33 @@ __device__ void decide_sequence(const CommitArgs& a, int b, bool write_unmasked,
     }
     if (!msk[p]) continue;
     ++nmask;
-    // merge the row's chunks in chunk order
-    const CommitChunk* c = a.chunks + row * a.n_chunks;
+    // merge the row's chunk records (written by the previous launch), eight at a time with
+    // all loads in flight, by an online max / lowest argmax / rescaled fp64 sum in chunk
+    // order (the rescale factors in fp32: relative error ~1e-7 on an estimate decided
+    // outside 1e-4)
+    const unsigned long long* c = reinterpret_cast<const unsigned long long*>(a.chunks + row * a.n_chunks);
     float M = -INFINITY;
     int tok = 0x7fffffff;
-#pragma unroll 1
-    for (int k = 0; k < a.n_chunks; ++k) argmax_merge(M, tok, c[k].m, c[k].tok);
     double Z = 0.0;
-#pragma unroll 1
-    for (int k = 0; k < a.n_chunks; ++k) Z += c[k].z * exp((double)c[k].m - (double)M);
+    for (int k0 = 0; k0 < a.n_chunks; k0 += 8) {
+      unsigned long long r[8], zb[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int k = min(k0 + j, a.n_chunks - 1);
+        r[j] = c[2 * k];
+        zb[j] = c[2 * k + 1];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (k0 + j >= a.n_chunks) break;
+        const float mk = __uint_as_float((uint32_t)r[j]);
+        const double zk = __longlong_as_double((long long)zb[j]);
+        const float mn = fmaxf(M, mk);
+        if (mk > M || (mk == M && (int)(uint32_t)(r[j] >> 32) < tok)) tok = (int)(uint32_t)(r[j] >> 32);
+        Z = Z * (double)__builtin_amdgcn_exp2f((M - mn) * kLog2e) + zk * (double)__builtin_amdgcn_exp2f((mk - mn) * kLog2e);
+        M = mn;
+      }
+    }
     mm[p] = M;
     tk[p] = tok;
     zz[p] = Z;
@@ -263,7 +279,7 @@ __device__ void decide_sequence(const CommitArgs& a, int b, bool write_unmasked,
   }
 }
 
-// ---- the commit: per-chunk reduction, then the sequence's last arrival decides -----------
+// ---- step 1: per-chunk reduction ------------------------------------------------------
 
 template <typename T>
 __global__ __launch_bounds__(NT) void commit_reduce_kernel(CommitArgs a) {
@@ -271,30 +287,11 @@ __global__ __launch_bounds__(NT) void commit_reduce_kernel(CommitArgs a) {
   __shared__ float sm_m[4];
   __shared__ int sm_t[4];
   __shared__ double sm_z[4];
-  __shared__ int sm_n[4];
-  __shared__ int sm_last;
-  __shared__ DecideSmem dsm;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int blk = blockIdx.x;
   const int row = blk / a.n_chunks;
   const int ch = blk - row * a.n_chunks;
-  if (!a.mask[row]) {
-    if (ch == 0 && tid == 0) {  // an unmasked row: its outputs, and nothing read
-      a.token_id[row] = -1;
-      a.committed[row] = 0;
-      if (a.conf) a.conf[row] = 0.0f;
-    }
-    return;
-  }
-  const int b = row / a.S;
-  // this thread's share of the sequence's mask (S <= 1024 = 4 per thread), loaded before
-  // the logits so that its wait does not hold them up
-  int nm = 0;
-#pragma unroll
-  for (int k = 0; k < 1024 / NT; ++k) {
-    const int i = tid + k * NT;
-    if (i < a.S) nm += a.mask[(size_t)b * a.S + i] != 0;
-  }
+  if (!a.mask[row]) return;  // an unmasked row is never read
   const T* base = static_cast<const T*>(a.logits) + (size_t)row * a.V;
   const int begin = ch * a.chunk_elems;
   const int end = min(a.V, begin + a.chunk_elems);
@@ -351,12 +348,10 @@ __global__ __launch_bounds__(NT) void commit_reduce_kernel(CommitArgs a) {
     const float m2 = __shfl_xor(m, off, 64);
     const int t2 = __shfl_xor(tok, off, 64);
     argmax_merge(m, tok, m2, t2);
-    nm += __shfl_xor(nm, off, 64);
   }
   if (lane == 0) {
     sm_m[w] = m;
     sm_t[w] = tok;
-    sm_n[w] = nm;
   }
   __syncthreads();
   float M = sm_m[0];
@@ -375,27 +370,10 @@ __global__ __launch_bounds__(NT) void commit_reduce_kernel(CommitArgs a) {
     c.tok = TOK;
     c.z = (sm_z[0] + sm_z[1]) + (sm_z[2] + sm_z[3]);
     a.chunks[(size_t)row * a.n_chunks + ch] = c;
-    // release the record, then count this chunk's arrival on the sequence's word
-    __threadfence();
-    const uint32_t total = (uint32_t)((sm_n[0] + sm_n[1]) + (sm_n[2] + sm_n[3])) * (uint32_t)a.n_chunks;
-    unsigned long long* word = a.arrivals + b;
-    unsigned long long seen = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    unsigned long long want, prev;
-    do {
-      prev = seen;
-      const uint32_t cnt = ((uint32_t)(prev >> 32) == a.tag) ? (uint32_t)prev + 1u : 1u;
-      want = ((unsigned long long)a.tag << 32) | cnt;
-      seen = atomicCAS(word, prev, want);
-    } while (seen != prev);
-    const int last = (uint32_t)want == total;
-    if (last) __hip_atomic_store(word, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sm_last = last;
   }
-  __syncthreads();
-  if (!sm_last) return;
-  __threadfence();  // acquire: every record of the sequence is visible from here
-  decide_sequence<T, NT>(a, b, false, dsm);
 }
+
+// ---- step 2: per-sequence decision -----------------------------------------------------
 
 template <typename T>
 __global__ __launch_bounds__(512) void commit_decide_kernel(CommitArgs a) {
@@ -412,12 +390,20 @@ hipError_t launch_commit_decide(const CommitArgs& a, hipStream_t s) {
 
 int commit_chunk_elems(int dtype) { return NT * LOADS * (dtype == TT_BF16 ? 8 : 4); }
 
-hipError_t launch_commit(const CommitArgs& a, hipStream_t s) {
+
+hipError_t launch_commit(const CommitArgs& a, hipStream_t s, hipEvent_t ev_reduce_end) {
   const long long nblk = (long long)a.B * a.S * a.n_chunks;
   if (a.dtype == TT_BF16)
     hipLaunchKernelGGL(commit_reduce_kernel<uint16_t>, dim3((unsigned)nblk), dim3(NT), 0, s, a);
   else
     hipLaunchKernelGGL(commit_reduce_kernel<float>, dim3((unsigned)nblk), dim3(NT), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (ev_reduce_end) (void)hipEventRecord(ev_reduce_end, s);
+  if (a.dtype == TT_BF16)
+    hipLaunchKernelGGL(commit_decide_kernel<uint16_t>, dim3(a.B), dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL(commit_decide_kernel<float>, dim3(a.B), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

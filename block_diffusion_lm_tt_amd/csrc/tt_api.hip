@@ -2,8 +2,6 @@
 // The operations themselves are documented in include/tt.h.
 #include <math.h>
 
-#include <atomic>
-#include <chrono>
 #include <mutex>
 #include <vector>
 
@@ -57,7 +55,7 @@ tt_status plan_attn(const tt_attn_shape* sh, AttnPlan* p) {
 
 struct CommitPlan {
   int n_chunks, chunk_elems;
-  size_t chunk_bytes, arrival_bytes;
+  size_t chunk_bytes;
 };
 
 tt_status plan_commit(int32_t B, int32_t S, int32_t V, int32_t dtype, CommitPlan* p) {
@@ -69,23 +67,7 @@ tt_status plan_commit(int32_t B, int32_t S, int32_t V, int32_t dtype, CommitPlan
   // one workgroup per (row, chunk): the launch grid bounds the shape
   if ((long long)B * S * p->n_chunks > kMaxGridBlocks) return TT_ERR_UNSUPPORTED;
   p->chunk_bytes = align_up((size_t)B * S * p->n_chunks * sizeof(CommitChunk));
-  p->arrival_bytes = align_up((size_t)B * sizeof(unsigned long long));
   return TT_OK;
-}
-
-// A nonzero 32-bit tag per commit call: a per-process salt (clock at first use) stepped by
-// a call counter through a 64-bit mixing function. Arrival words left by earlier calls, or
-// any other stale workspace contents, carry another tag and count as zero.
-uint32_t next_commit_tag() {
-  static const uint64_t salt =
-      (uint64_t)std::chrono::high_resolution_clock::now().time_since_epoch().count();
-  static std::atomic<uint64_t> calls{0};
-  uint64_t x = salt + 0x9E3779B97F4A7C15ull * (calls.fetch_add(1) + 1);
-  x = (x ^ (x >> 30)) * 0xBF58476D1CE4E5B9ull;
-  x = (x ^ (x >> 27)) * 0x94D049BB133111EBull;
-  x ^= x >> 31;
-  const uint32_t t = (uint32_t)x ^ (uint32_t)(x >> 32);
-  return t ? t : 1u;
 }
 
 struct LmPlan {
@@ -112,7 +94,7 @@ struct Profiler {
   std::mutex mu;
   bool enabled = false;
   std::vector<hipEvent_t> attn_ev[4];   // attn start, main start, main end, attn end
-  std::vector<hipEvent_t> commit_ev[2]; // commit start, commit end (one kernel)
+  std::vector<hipEvent_t> commit_ev[3]; // commit start, reduce end, commit end
   std::vector<hipEvent_t> lm_ev[3];     // LM-head commit start, reduce end, end
   int64_t attn_calls = 0, commit_calls = 0, lm_calls = 0;
   int attn_used = 0, commit_used = 0, lm_used = 0;
@@ -226,7 +208,7 @@ tt_status tt_block_denoise_attn(const tt_attn_shape* shape, const void* q, const
 size_t tt_commit_workspace(int32_t B, int32_t S, int32_t V, int32_t dtype) {
   CommitPlan p;
   if (plan_commit(B, S, V, dtype, &p) != TT_OK) return 0;
-  const size_t n = p.chunk_bytes + p.arrival_bytes;
+  const size_t n = p.chunk_bytes;
   return n < kAlign ? kAlign : n;
 }
 
@@ -251,8 +233,6 @@ tt_status tt_commit(int32_t B, int32_t S, int32_t V, int32_t dtype, const void* 
   a.conf = conf;
   char* ws = static_cast<char*>(workspace);
   a.chunks = reinterpret_cast<CommitChunk*>(ws);
-  a.arrivals = reinterpret_cast<unsigned long long*>(ws + p.chunk_bytes);
-  a.tag = next_commit_tag();
   a.B = B;
   a.S = S;
   a.V = V;
@@ -260,21 +240,21 @@ tt_status tt_commit(int32_t B, int32_t S, int32_t V, int32_t dtype, const void* 
   a.chunk_elems = p.chunk_elems;
   a.dtype = dtype;
 
-  hipEvent_t ev[2] = {nullptr, nullptr};
+  hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
   {
     std::lock_guard<std::mutex> lk(g_prof.mu);
     if (g_prof.enabled) {
       ++g_prof.commit_calls;
       if (g_prof.commit_used < kMaxTimed) {
-        for (int k = 0; k < 2; ++k) ev[k] = ev_slot(g_prof.commit_ev[k], g_prof.commit_used);
-        if (ev[0] && ev[1]) ++g_prof.commit_used;
-        else ev[0] = ev[1] = nullptr;
+        for (int k = 0; k < 3; ++k) ev[k] = ev_slot(g_prof.commit_ev[k], g_prof.commit_used);
+        if (ev[0] && ev[1] && ev[2]) ++g_prof.commit_used;
+        else ev[0] = ev[1] = ev[2] = nullptr;
       }
     }
   }
   if (ev[0]) (void)hipEventRecord(ev[0], stream);
-  hipError_t e = launch_commit(a, stream);
-  if (ev[1]) (void)hipEventRecord(ev[1], stream);
+  hipError_t e = launch_commit(a, stream, ev[1]);
+  if (ev[2]) (void)hipEventRecord(ev[2], stream);
   return e == hipSuccess ? TT_OK : TT_ERR_HIP;
 }
 
@@ -319,8 +299,6 @@ tt_status tt_lmhead_commit(int32_t B, int32_t S, int32_t K, int32_t V, const voi
   c.committed = committed;
   c.conf = conf;
   c.chunks = l.merged;
-  c.arrivals = nullptr;  // the separate decide launch counts no arrivals
-  c.tag = 0;
   c.B = B;
   c.S = S;
   c.V = V;
@@ -407,10 +385,11 @@ tt_status tt_profile_read(tt_profile_stats* out) {
     s.attn_main_ms += ms;
   }
   for (int k = 0; k < g_prof.commit_used; ++k) {
-    if (hipEventSynchronize(g_prof.commit_ev[1][k]) != hipSuccess) return TT_ERR_HIP;
-    if (hipEventElapsedTime(&ms, g_prof.commit_ev[0][k], g_prof.commit_ev[1][k]) != hipSuccess) return TT_ERR_HIP;
+    if (hipEventSynchronize(g_prof.commit_ev[2][k]) != hipSuccess) return TT_ERR_HIP;
+    if (hipEventElapsedTime(&ms, g_prof.commit_ev[0][k], g_prof.commit_ev[2][k]) != hipSuccess) return TT_ERR_HIP;
     s.commit_total_ms += ms;
-    s.commit_reduce_ms += ms;  // the reduction and the decisions are one kernel
+    if (hipEventElapsedTime(&ms, g_prof.commit_ev[0][k], g_prof.commit_ev[1][k]) != hipSuccess) return TT_ERR_HIP;
+    s.commit_reduce_ms += ms;
   }
   for (int k = 0; k < g_prof.lm_used; ++k) {
     if (hipEventSynchronize(g_prof.lm_ev[2][k]) != hipSuccess) return TT_ERR_HIP;

@@ -67,8 +67,6 @@ struct CommitArgs {
   uint8_t* committed;
   float* conf;
   CommitChunk* chunks;     // [B*S][n_chunks]
-  unsigned long long* arrivals;  // [B] per-sequence arrival words: (tag << 32) | count
-  uint32_t tag;            // this call's nonzero tag
   int B, S, V;
   int n_chunks, chunk_elems;
   int dtype;
@@ -96,8 +94,9 @@ hipError_t launch_ctx_append(const AppendArgs& a, hipStream_t s);
 
 int commit_chunk_elems(int dtype);
 constexpr long long kMaxGridBlocks = 16777215;  // 256-thread workgroups: < 2^32 work-items
-// the commit (one launch: chunk reduction, then each sequence decided by its last arrival)
-hipError_t launch_commit(const CommitArgs& a, hipStream_t s);
+// the commit: the chunk reduction, then the per-sequence decision (an event may be recorded
+// between the two launches)
+hipError_t launch_commit(const CommitArgs& a, hipStream_t s, hipEvent_t ev_reduce_end);
 // the decide step alone (a.logits == nullptr: decisions on the chunk estimates only)
 hipError_t launch_commit_decide(const CommitArgs& a, hipStream_t s);
 

@@ -129,10 +129,8 @@ tt_status tt_block_denoise_attn(const tt_attn_shape *shape, const void *q, const
  *   conf       [B, S]      float, may be NULL      (device, written)
  *
  *   workspace  device memory of tt_commit_workspace(B, S, V, dtype) bytes: 16 bytes per
- *              (position, vocabulary chunk of 16384 bf16 / 8192 fp32 entries) and 8 per
- *              sequence (an arrival word tagged per call). Its contents on entry are
- *              ignored: words left by other calls or other users carry another tag (a
- *              stale word equals this call's 32-bit tag with probability 2^-32).
+ *              (position, vocabulary chunk of 16384 bf16 / 8192 fp32 entries); contents on
+ *              entry are ignored.
  *
  * Supported: dtype TT_BF16 or TT_F32, 1 <= S <= 1024, 1 <= V, and B*S*ceil(V/chunk) <=
  * 16777215 (one workgroup per position and chunk); anything else returns
@@ -228,8 +226,7 @@ typedef struct {
     double attn_main_ms;      /* sum over those calls, the main attention kernel alone   */
     int64_t commit_calls;     /* tt_commit calls timed                                   */
     double commit_total_ms;   /* sum over those calls, first launch to last              */
-    double commit_reduce_ms;  /* sum over those calls, the commit's kernel (one launch:   */
-                              /* the vocabulary reduction, then the decisions)           */
+    double commit_reduce_ms;  /* sum over those calls, the vocabulary reduction kernel   */
     int64_t lm_calls;         /* tt_lmhead_commit calls timed                            */
     double lm_total_ms;       /* sum over those calls, first launch to last              */
     double lm_reduce_ms;      /* sum over those calls, the fused head + reduction kernel */
