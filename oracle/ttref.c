@@ -25,7 +25,13 @@
  *     distribution at temperature 1; the token is the lowest index attaining the max;
  *   - "above the threshold" is strict (conf > gamma);
  *   - if a sequence has masked positions but none clears gamma, its single most
- *     confident masked position is committed (ties: lowest position).
+ *     confident masked position is committed (ties: lowest position);
+ *   - the denoiser's Mamba-2 scan is the Mamba-2 selective state-space recurrence (the
+ *     pages name the layer type, not its equations), causal, started from the state seeded
+ *     by the context tower;
+ *   - adaLN is layer normalization without affine terms followed by (1 + scale) and shift,
+ *     and a gated residual, with each layer's vectors the sum of one shared set per
+ *     sequence (from the timestep) and the layer's own learned offsets ("adaLN-single").
  *
  * Parity pins: every function here is checked against library routines, closed forms
  * and invariants by the CPU test suite; no function is left unpinned.
@@ -334,5 +340,147 @@ int ttref_ctx_append(int B, int S, int Hkv, int D, int Lmax, int dtype, const vo
         if (bump)
             ctx_len[b] = n + S;
     }
+    return TTREF_OK;
+}
+
+/*
+ * Mamba-2 layer of the denoiser over one block, started from the seeded state ([SN] "Hvad
+ * TwoTower aendrer teknisk": the denoiser's Mamba-2 states are seeded directly from the
+ * context tower; [GS] Methodology > Architecture: the context tower produces the KV caches and
+ * Mamba states; [GS] ablations: the final design keeps Mamba causal). The scan is the Mamba-2
+ * selective state-space recurrence, per sequence b and head h (H heads of width P, state
+ * width N, G groups of heads sharing B and C, group of head h = h / (H/G)):
+ *
+ *   delta_t = softplus(dt[b,t,h] + dt_bias[h]),   A_h = -exp(A_log[h]),   a_t = exp(delta_t A_h)
+ *   state_t[p][n] = a_t state_{t-1}[p][n] + delta_t x[b,t,h,p] B[b,t,g,n]
+ *   y[b,t,h,p]   = sum_n state_t[p][n] C[b,t,g,n] + D[h] x[b,t,h,p]
+ *
+ * for t = 0..S-1 in order, from state_{-1} = h0[b,h] (the seeded state). The state after the
+ * block goes to h_out when it is given (the context tower's own state update over a committed
+ * block is the same recurrence). x, B, C are bf16 bits or fp32 (dtype); dt, dt_bias, A_log,
+ * D and the states are fp32; y and h_out are double. softplus(z) = log(1 + e^z).
+ * Layouts: x, y [B,S,H,P]; dt [B,S,H]; B, C [B,S,G,N]; h0, h_out [B,H,P,N].
+ */
+static double ttref_softplus(double z)
+{
+    return z > 30.0 ? z : log1p(exp(z));
+}
+
+int ttref_mamba2_scan(int B, int S, int H, int P, int N, int G, int dtype, const void *x,
+                      const float *dt, const float *dt_bias, const float *A_log, const float *Dskip,
+                      const void *Bm, const void *Cm, const float *h0, double *y, double *h_out)
+{
+    if (B < 0 || S < 1 || H < 1 || P < 1 || N < 1 || G < 1 || H % G != 0)
+        return TTREF_EINVAL;
+    if (dtype != TTREF_F32 && dtype != TTREF_BF16)
+        return TTREF_EINVAL;
+    const int hpg = H / G;
+    int failed = 0;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h) {
+            const int g = h / hpg;
+            double *st = (double *)malloc((size_t)P * N * sizeof(double));
+            if (!st) {
+#pragma omp atomic write
+                failed = 1;
+                continue;
+            }
+            const size_t soff = ((size_t)b * H + h) * P * N;
+            for (size_t k = 0; k < (size_t)P * N; ++k)
+                st[k] = (double)h0[soff + k];
+            const double A = -exp((double)A_log[h]);
+            for (int t = 0; t < S; ++t) {
+                const double delta = ttref_softplus((double)dt[((size_t)b * S + t) * H + h] + (double)dt_bias[h]);
+                const double a = exp(delta * A);
+                const size_t xoff = (((size_t)b * S + t) * H + h) * P;
+                const size_t boff = (((size_t)b * S + t) * G + g) * N;
+                for (int p = 0; p < P; ++p) {
+                    const double xp = ttref_load(x, xoff + p, dtype);
+                    double acc = 0.0;
+                    for (int n = 0; n < N; ++n) {
+                        double *s = st + (size_t)p * N + n;
+                        *s = a * *s + delta * xp * ttref_load(Bm, boff + n, dtype);
+                        acc += *s * ttref_load(Cm, boff + n, dtype);
+                    }
+                    y[xoff + p] = acc + (double)Dskip[h] * xp;
+                }
+            }
+            if (h_out)
+                for (size_t k = 0; k < (size_t)P * N; ++k)
+                    h_out[soff + k] = st[k];
+            free(st);
+        }
+    return failed ? TTREF_ENOMEM : TTREF_OK;
+}
+
+/*
+ * adaLN-single time modulation of one denoiser layer ([GS] Training and Conditioning > Time
+ * Conditioning: the denoiser is conditioned on the diffusion timestep t through adaptive
+ * layer normalization; [SN] "Hvad TwoTower aendrer teknisk": every layer is time-modulated by
+ * a small adaLN-single block). The single block maps a sequence's timestep to one set of
+ * modulation vectors t_mod[b] = (shift, scale, gate), shared by all layers; each layer adds
+ * its own learned offsets table = (shift, scale, gate). For a row x[b,i,0:d]:
+ *
+ *   u = (x - mean(x)) / sqrt(var(x) + eps)         (layer normalization, no affine terms;
+ *                                                   var is the mean of squared deviations)
+ *   y = u * (1 + scale) + shift                     (adaln_modulate, before the layer's mixer)
+ *   out = x + gate * f                              (adaln_gate: the mixer's output f joins
+ *                                                    the residual stream)
+ *
+ * with shift = t_mod[b,0,:] + table[0,:], scale = t_mod[b,1,:] + table[1,:], gate =
+ * t_mod[b,2,:] + table[2,:]. x and f are bf16 bits or fp32 (dtype); t_mod [B,3,d] and table
+ * [3,d] fp32; y and out double [B,S,d].
+ */
+int ttref_adaln_modulate(int B, int S, int d, int dtype, const void *x, const float *t_mod,
+                         const float *table, double eps, double *y)
+{
+    if (B < 0 || S < 1 || d < 1 || !(eps >= 0.0))
+        return TTREF_EINVAL;
+    if (dtype != TTREF_F32 && dtype != TTREF_BF16)
+        return TTREF_EINVAL;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int b = 0; b < B; ++b)
+        for (int i = 0; i < S; ++i) {
+            const size_t off = ((size_t)b * S + i) * d;
+            double mean = 0.0;
+            for (int k = 0; k < d; ++k)
+                mean += ttref_load(x, off + k, dtype);
+            mean /= d;
+            double var = 0.0;
+            for (int k = 0; k < d; ++k) {
+                const double e = ttref_load(x, off + k, dtype) - mean;
+                var += e * e;
+            }
+            var /= d;
+            const double rstd = 1.0 / sqrt(var + eps);
+            const float *tm = t_mod + (size_t)b * 3 * d;
+            for (int k = 0; k < d; ++k) {
+                const double shift = (double)tm[k] + (double)table[k];
+                const double scale = (double)tm[d + k] + (double)table[d + k];
+                const double u = (ttref_load(x, off + k, dtype) - mean) * rstd;
+                y[off + k] = u * (1.0 + scale) + shift;
+            }
+        }
+    return TTREF_OK;
+}
+
+int ttref_adaln_gate(int B, int S, int d, int dtype, const void *x, const void *f,
+                     const float *t_mod, const float *table, double *out)
+{
+    if (B < 0 || S < 1 || d < 1)
+        return TTREF_EINVAL;
+    if (dtype != TTREF_F32 && dtype != TTREF_BF16)
+        return TTREF_EINVAL;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int b = 0; b < B; ++b)
+        for (int i = 0; i < S; ++i) {
+            const size_t off = ((size_t)b * S + i) * d;
+            const float *tm = t_mod + (size_t)b * 3 * d;
+            for (int k = 0; k < d; ++k) {
+                const double gate = (double)tm[2 * d + k] + (double)table[2 * d + k];
+                out[off + k] = ttref_load(x, off + k, dtype) + gate * ttref_load(f, off + k, dtype);
+            }
+        }
     return TTREF_OK;
 }

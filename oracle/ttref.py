@@ -39,6 +39,12 @@ def _lib():
         L.ttref_lmhead_commit.restype = i32
         L.ttref_ctx_append.argtypes = [i32] * 6 + [vp] * 5 + [i32, vp]
         L.ttref_ctx_append.restype = i32
+        L.ttref_mamba2_scan.argtypes = [i32] * 7 + [vp] * 10
+        L.ttref_mamba2_scan.restype = i32
+        L.ttref_adaln_modulate.argtypes = [i32] * 4 + [vp] * 3 + [ctypes.c_double, vp]
+        L.ttref_adaln_modulate.restype = i32
+        L.ttref_adaln_gate.argtypes = [i32] * 4 + [vp] * 5
+        L.ttref_adaln_gate.restype = i32
         L.ttref_threads.argtypes = []
         L.ttref_threads.restype = i32
         _LIB = L
@@ -136,3 +142,54 @@ def ttref_ctx_append(B, S, Hkv, D, Lmax, dtype, k_new, v_new, k_ctx, v_ctx, ctx_
     if rc != 0:
         raise ValueError(f"ttref_ctx_append failed with status {rc}")
     return kc, vc, ctx, skipped
+
+
+def _f32(a, n):
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    assert a.size == n
+    return a
+
+
+def ttref_mamba2_scan(B, S, H, P, N, G, dtype, x, dt, dt_bias, A_log, Dskip, Bm, Cm, h0, want_state=True):
+    """Mamba-2 scan of one block from the seeded state h0. x [B,S,H,P] and Bm, Cm [B,S,G,N] in
+    dtype (bf16 bits or fp32); dt [B,S,H], dt_bias, A_log, Dskip [H] and h0 [B,H,P,N] fp32.
+    Returns (y f64 [B,S,H,P], h_out f64 [B,H,P,N] or None)."""
+    for t in (x, Bm, Cm):
+        _check_dtype(t, dtype)
+    assert x.size == B * S * H * P and Bm.size == B * S * G * N and Cm.size == Bm.size
+    dt, dt_bias, A_log, Dskip = _f32(dt, B * S * H), _f32(dt_bias, H), _f32(A_log, H), _f32(Dskip, H)
+    h0 = _f32(h0, B * H * P * N)
+    y = np.zeros((B, S, H, P), dtype=np.float64)
+    hs = np.zeros((B, H, P, N), dtype=np.float64) if want_state else None
+    rc = _lib().ttref_mamba2_scan(B, S, H, P, N, G, _DT[dtype], _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A_log),
+                                  _ptr(Dskip), _ptr(Bm), _ptr(Cm), _ptr(h0), _ptr(y),
+                                  _ptr(hs) if hs is not None else None)
+    if rc != 0:
+        raise ValueError(f"ttref_mamba2_scan failed with status {rc}")
+    return y, hs
+
+
+def ttref_adaln_modulate(B, S, d, dtype, x, t_mod, table, eps=1e-6):
+    """adaLN modulation before a layer's mixer: LN(x) * (1 + scale) + shift. x [B,S,d] in dtype,
+    t_mod [B,3,d] and table [3,d] fp32 (shift, scale, gate). Returns y f64 [B,S,d]."""
+    _check_dtype(x, dtype)
+    assert x.size == B * S * d
+    t_mod, table = _f32(t_mod, B * 3 * d), _f32(table, 3 * d)
+    y = np.zeros((B, S, d), dtype=np.float64)
+    rc = _lib().ttref_adaln_modulate(B, S, d, _DT[dtype], _ptr(x), _ptr(t_mod), _ptr(table), float(eps), _ptr(y))
+    if rc != 0:
+        raise ValueError(f"ttref_adaln_modulate failed with status {rc}")
+    return y
+
+
+def ttref_adaln_gate(B, S, d, dtype, x, f, t_mod, table):
+    """Gated residual after a layer's mixer: x + gate * f. Returns out f64 [B,S,d]."""
+    _check_dtype(x, dtype)
+    _check_dtype(f, dtype)
+    assert x.size == B * S * d and f.size == x.size
+    t_mod, table = _f32(t_mod, B * 3 * d), _f32(table, 3 * d)
+    out = np.zeros((B, S, d), dtype=np.float64)
+    rc = _lib().ttref_adaln_gate(B, S, d, _DT[dtype], _ptr(x), _ptr(f), _ptr(t_mod), _ptr(table), _ptr(out))
+    if rc != 0:
+        raise ValueError(f"ttref_adaln_gate failed with status {rc}")
+    return out

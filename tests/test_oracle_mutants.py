@@ -4,8 +4,12 @@ Each case copies oracle/ttref.c, applies one plausible slip (a dropped scale, a 
 sign, a wrong KV-head index, a transposed layout, values read from K, a dropped block key,
 >= instead of >, a wrong tie rule, a missing fallback, a cache update at the wrong rows,
 without the length bump or with an off-by-one fit test, an LM head read transposed, from
-the wrong sequence, short of its last feature or with a flipped product), builds that copy into a temporary
-library and runs the pin suite against it in a child process. The suite must fail.
+the wrong sequence, short of its last feature or with a flipped product; a Mamba-2 scan with a
+flipped decay, no softplus, no skip term, a wrong head-to-group map, an unseeded state, the
+update reading C, the readout before the update or the decay applied to the new input; an
+adaLN without the mean, without the 1 +, with shift and scale or gate slots mixed up, without
+the layer's offsets or with eps outside the root), builds that copy into a temporary library
+and runs both pin suites against it in a child process. The suites must fail.
 """
 import os
 import subprocess
@@ -44,6 +48,33 @@ MUTANTS = {
     "append_fit_off_by_one": ("(long long)n + S > Lmax", "(long long)n + S >= Lmax"),
     "append_values_from_keys": ("memcpy((char *)v_ctx + dst, (const char *)v_new + src, row);",
                                 "memcpy((char *)v_ctx + dst, (const char *)k_new + src, row);"),
+    # the denoiser's Mamba-2 scan from the seeded state
+    "mamba_decay_sign": ("const double A = -exp((double)A_log[h]);", "const double A = exp((double)A_log[h]);"),
+    "mamba_no_softplus": ("const double delta = ttref_softplus(", "const double delta = ("),
+    "mamba_no_skip": ("y[xoff + p] = acc + (double)Dskip[h] * xp;", "y[xoff + p] = acc;"),
+    "mamba_group_modulo": ("const int g = h / hpg;", "const int g = h % G;"),
+    "mamba_unseeded": ("st[k] = (double)h0[soff + k];", "st[k] = 0.0;"),
+    "mamba_update_reads_c": ("*s = a * *s + delta * xp * ttref_load(Bm, boff + n, dtype);",
+                             "*s = a * *s + delta * xp * ttref_load(Cm, boff + n, dtype);"),
+    "mamba_readout_before_update": (
+        "*s = a * *s + delta * xp * ttref_load(Bm, boff + n, dtype);\n"
+        "                        acc += *s * ttref_load(Cm, boff + n, dtype);",
+        "acc += *s * ttref_load(Cm, boff + n, dtype);\n"
+        "                        *s = a * *s + delta * xp * ttref_load(Bm, boff + n, dtype);"),
+    "mamba_decay_on_input": ("*s = a * *s + delta * xp * ttref_load(Bm, boff + n, dtype);",
+                             "*s = a * (*s + delta * xp * ttref_load(Bm, boff + n, dtype));"),
+    # adaLN-single modulation and gated residual
+    "adaln_no_mean": ("const double e = ttref_load(x, off + k, dtype) - mean;",
+                      "const double e = ttref_load(x, off + k, dtype);"),
+    "adaln_no_one_plus": ("y[off + k] = u * (1.0 + scale) + shift;", "y[off + k] = u * scale + shift;"),
+    "adaln_shift_from_scale_slot": ("const double shift = (double)tm[k] + (double)table[k];",
+                                    "const double shift = (double)tm[d + k] + (double)table[d + k];"),
+    "adaln_no_layer_table": ("const double scale = (double)tm[d + k] + (double)table[d + k];",
+                             "const double scale = (double)tm[d + k];"),
+    "adaln_eps_outside_root": ("const double rstd = 1.0 / sqrt(var + eps);",
+                               "const double rstd = 1.0 / (sqrt(var) + eps);"),
+    "adaln_gate_slot": ("const double gate = (double)tm[2 * d + k] + (double)table[2 * d + k];",
+                        "const double gate = (double)tm[d + k] + (double)table[d + k];"),
 }
 
 
@@ -59,7 +90,8 @@ def test_pins_catch_planted_mistake(name, tmp_path):
                     str(lib), "-lm"], check=True)
     env = dict(os.environ, TTREF_LIB=str(lib), OMP_NUM_THREADS="2")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_pins_f4.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout[-2000:]}"
     assert "failed" in r.stdout, r.stdout[-2000:] + r.stderr[-2000:]
