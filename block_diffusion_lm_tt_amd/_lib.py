@@ -78,6 +78,8 @@ def lib() -> ctypes.CDLL:
         L.tt_commit_workspace.argtypes = [i32, i32, i32, i32]
         L.tt_commit.restype = i32
         L.tt_commit.argtypes = [i32, i32, i32, i32, vp, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp]
+        L.tt_commit_noalloc.restype = i32
+        L.tt_commit_noalloc.argtypes = [i32, i32, i32, i32, vp, vp, ctypes.c_float, vp, vp, vp, vp]
         L.tt_lmhead_commit_workspace.restype = sz
         L.tt_lmhead_commit_workspace.argtypes = [i32, i32, i32, i32]
         L.tt_lmhead_commit.restype = i32

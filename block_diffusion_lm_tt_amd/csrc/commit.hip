@@ -30,6 +30,8 @@
 //  Folding step 2 into step 1 (the last-arriving workgroup of a sequence deciding) was built
 //  and measured slower: the arrival counters are device-scope atomics on one word per
 //  sequence, about 80 per word here, and they serialize (49.6 us per call against 25).
+#include <mutex>
+
 #include "tt_internal.h"
 
 namespace tt {
@@ -390,6 +392,30 @@ hipError_t launch_commit_decide(const CommitArgs& a, hipStream_t s) {
 
 int commit_chunk_elems(int dtype) { return NT * LOADS * (dtype == TT_BF16 ? 8 : 4); }
 
+// ---- scratch of the allocation-free commit entry point ---------------------------------
+// One array per GPU, held until the process ends; every allocation-free commit call on a GPU
+// uses that GPU's copy (calls that overlap on one GPU race on it). In host code the array's
+// name is only a stand-in: its device address is looked up once per device and kept.
+static __device__ __align__(256) unsigned char scratch[kCommitScratchBytes];
+
+hipError_t commit_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_commit(const CommitArgs& a, hipStream_t s, hipEvent_t ev_reduce_end) {
   const long long nblk = (long long)a.B * a.S * a.n_chunks;

@@ -258,6 +258,36 @@ tt_status tt_commit(int32_t B, int32_t S, int32_t V, int32_t dtype, const void* 
   return e == hipSuccess ? TT_OK : TT_ERR_HIP;
 }
 
+tt_status tt_commit_noalloc(int32_t B, int32_t S, int32_t V, int32_t dtype, const void* logits,
+                            const uint8_t* mask, float gamma, int32_t* token_id, uint8_t* committed,
+                            float* conf, hipStream_t stream) {
+  CommitPlan p;
+  tt_status st = plan_commit(B, S, V, dtype, &p);
+  if (st != TT_OK) return st;
+  if (isnan(gamma)) return TT_ERR_INVALID_ARG;
+  if (B == 0) return TT_OK;
+  if (!logits || !mask || !token_id || !committed) return TT_ERR_INVALID_ARG;
+  if (p.chunk_bytes > kCommitScratchBytes) return TT_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  if (commit_scratch(&ws) != hipSuccess) return TT_ERR_HIP;
+
+  CommitArgs a;
+  a.logits = logits;
+  a.mask = mask;
+  a.gamma = gamma;
+  a.token_id = token_id;
+  a.committed = committed;
+  a.conf = conf;
+  a.chunks = static_cast<CommitChunk*>(ws);
+  a.B = B;
+  a.S = S;
+  a.V = V;
+  a.n_chunks = p.n_chunks;
+  a.chunk_elems = p.chunk_elems;
+  a.dtype = dtype;
+  return launch_commit(a, stream, nullptr) == hipSuccess ? TT_OK : TT_ERR_HIP;
+}
+
 size_t tt_lmhead_commit_workspace(int32_t B, int32_t S, int32_t K, int32_t V) {
   LmPlan p;
   if (plan_lmhead(B, S, K, V, &p) != TT_OK) return 0;

@@ -99,6 +99,10 @@ constexpr long long kMaxGridBlocks = 16777215;  // 256-thread workgroups: < 2^32
 hipError_t launch_commit(const CommitArgs& a, hipStream_t s, hipEvent_t ev_reduce_end);
 // the decide step alone (a.logits == nullptr: decisions on the chunk estimates only)
 hipError_t launch_commit_decide(const CommitArgs& a, hipStream_t s);
+// The allocation-free commit's scratch: a static device array of this many bytes per GPU;
+// commit_scratch() returns the current device's address of it (looked up on first use).
+constexpr size_t kCommitScratchBytes = (size_t)4 << 20;
+hipError_t commit_scratch(void** ptr);
 
 // ---------------------------------------------------------------------------------------
 // LM head fused with the commit's vocabulary reduction

@@ -143,6 +143,23 @@ tt_status tt_commit(int32_t B, int32_t S, int32_t V, int32_t dtype, const void *
                     float *conf, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------
+ * tt_commit_noalloc -- tt_commit without a workspace argument, for callers that cannot
+ * allocate device memory (code under graph capture, serving loops that must not allocate,
+ * harnesses that forbid it). Same operation, arguments, results and kernels as tt_commit;
+ * the scratch is the library's own static device array of 4 MiB per GPU (allocated with the
+ * library's code object, held until the process ends), so the call allocates nothing.
+ *
+ * Limit: tt_commit_workspace(B, S, V, dtype) <= 4 MiB (e.g. B*S <= 16384 rows of a
+ * 131072-entry bf16 vocabulary); larger shapes return TT_ERR_UNSUPPORTED. Nothing in the
+ * array has to start at zero (each call writes every record it reads).
+ * Every call on one GPU uses that GPU's single array: calls that may overlap on one GPU
+ * (other streams, other threads) race and must be serialized by the caller.
+ * ------------------------------------------------------------------------------------- */
+tt_status tt_commit_noalloc(int32_t B, int32_t S, int32_t V, int32_t dtype, const void *logits,
+                            const uint8_t *mask, float gamma, int32_t *token_id,
+                            uint8_t *committed, float *conf, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------
  * tt_lmhead_commit -- the LM head and the confidence commit of one denoising step, fused:
  * the logits are never written to memory.
  *
