@@ -360,6 +360,103 @@ def lmhead_bench(args, torch, tt, TZ, W):
     print(json.dumps(res), flush=True)
 
 
+def mamba_bench(args, torch, tt, TZ, W):
+    """The denoiser's Mamba-2 scan from the context tower's seeded state (tt_mamba2_seeded_scan)
+    at the batched-serving shape: B=32 sequences, block S=16, d_model 4096 expanded twice to 128
+    heads of P=64, state size N=128, 8 B/C groups, bf16 activations and an fp32 state; the
+    per-step call of a denoising step (the state after the block is not written). Timed beside
+    it: the adaLN-single modulation and gated residual at d=4096 over the same B*S positions.
+    The seeded states and inputs rotate over several copies so that the last-level cache cannot
+    serve them. Prints one JSON line (an extra line, not the headline)."""
+    dev = torch.device("cuda:0")
+    B, S, H, P, N, G, d = 32, 16, 128, 64, 128, 8, 4096
+    log(f"[mamba] generating B={B} S={S} H={H} P={P} N={N} G={G}")
+    m = W.make_mamba(B, S, H, P, N, G, W.BF16, seed=1003)
+    base = TZ.mamba_to_device(m, dev)
+    R = max(1, args.rotate)
+    sets = [base] + [tuple(t.clone() for t in base) for _ in range(R - 1)]
+    y = torch.empty_like(base[0])
+    h_out = torch.empty_like(base[7])
+    a = W.make_adaln(B, S, d, W.BF16, seed=1003)
+    ax, af, atm, atab = TZ.adaln_to_device(a, dev)
+    asets = [(ax, af)] + [(ax.clone(), af.clone()) for _ in range(R - 1)]
+    ay = torch.empty_like(ax)
+
+    def timed(fn, reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for k in range(reps):
+            fn(k)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    scan = lambda k: tt.tt_mamba2_seeded_scan(*sets[k % R], G=G, y=y)  # noqa: E731
+    scan_state = lambda k: tt.tt_mamba2_seeded_scan(*sets[k % R], G=G, y=y, h_out=h_out)  # noqa: E731
+    modulate = lambda k: tt.tt_adaln_modulate(asets[k % R][0], atm, atab, y=ay)  # noqa: E731
+    gate = lambda k: tt.tt_adaln_gate(asets[k % R][0], asets[k % R][1], atm, atab, out=ay)  # noqa: E731
+    reps = max(20, args.steps)
+    for fn in (scan, scan_state, modulate, gate):
+        timed(fn, max(4, args.warmup))
+    t_scan = timed(scan, reps)
+    t_state = timed(scan_state, reps)
+    t_mod = timed(modulate, reps)
+    t_gate = timed(gate, reps)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for k in range(reps):
+        scan(k)
+        evs[k + 1].record()
+    torch.cuda.synchronize()
+    per = np.array([evs[k].elapsed_time(evs[k + 1]) * 1e3 for k in range(reps)])
+    p10, p50, p90 = (float(np.percentile(per, p)) for p in (10, 50, 90))
+
+    state_bytes = B * H * P * N * 4
+    act = 2  # bf16
+    io_bytes = (2 * B * S * H * P * act + 2 * B * S * G * N * act + B * S * H * 4 + 3 * H * 4)
+    alg = state_bytes + io_bytes
+    gbs = alg / t_scan / 1e9
+    flop = 2.0 * B * H * S * P * N  # the readout of the seeded state, the arithmetic bulk
+    ad_mod = 2 * B * S * d * act + (B * 3 * d + 3 * d) * 4
+    ad_gate = 3 * B * S * d * act + (B * 3 * d + 3 * d) * 4
+    log(f"[mamba] scan {t_scan*1e6:.1f} us/call (p10/p50/p90 {p10:.1f}/{p50:.1f}/{p90:.1f}; {gbs:.0f} GB/s), "
+        f"with the state written {t_state*1e6:.1f} us; adaLN modulate {t_mod*1e6:.1f} us, gate {t_gate*1e6:.1f} us")
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import ttref_mamba2_scan, ttref_threads
+        done, t_total = 0, 0.0
+        budget = min(args.cpu_budget, 15.0)
+        while t_total < budget:
+            t0 = time.perf_counter()
+            ttref_mamba2_scan(B, S, H, P, N, G, m.dtype, m.x, m.dt, m.dt_bias, m.A_log, m.Dskip, m.Bm, m.Cm, m.h0,
+                              want_state=False)
+            t_total += time.perf_counter() - t0
+            done += 1
+        cpu = {"value": done * B / t_total, "unit": "sequence-layers/s", "cores": ttref_threads(),
+               "kind": "oracle", "sample": f"{done} whole-batch scans of the timed shape, {t_total:.1f} s"}
+        log(f"[mamba] cpu baseline {cpu['value']:.1f} sequence-layers/s on {cpu['cores']} threads")
+    res = {"metric": "denoiser Mamba-2 block scans from the seeded state: sequence-layers per second",
+           "unit": "sequence-layers/s", "value": B / t_scan, "n_gpus": 1, "steps": reps,
+           "warmup": max(4, args.warmup), "ms_per_step": t_scan * 1e3, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded; N(0,1) inputs, N(0,1/N) B and C, N(0,0.5^2) seeded state)",
+           "config": {"workload": "denoiser Mamba-2 layer, batched serving", "B": B, "S": S, "H": H, "P": P,
+                      "N": N, "G": G, "d_model": d, "rotated_copies": R},
+           "scan_us_per_call": t_scan * 1e6, "scan_us_p10_p50_p90": [p10, p50, p90],
+           "scan_with_state_out_us_per_call": t_state * 1e6,
+           "scan_with_state_out_GBps": (alg + state_bytes) / t_state / 1e9,
+           "adaln_modulate_us_per_call": t_mod * 1e6, "adaln_modulate_GBps": ad_mod / t_mod / 1e9,
+           "adaln_gate_us_per_call": t_gate * 1e6, "adaln_gate_GBps": ad_gate / t_gate / 1e9,
+           "roofline": {"kernel": "mamba2_scan_kernel", "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None, "avg_us": t_scan * 1e6,
+                        "algorithmic_bytes_per_launch": alg, "fp32_flop_per_launch": flop,
+                        "fp32_frac": flop / t_scan / 1e12 / 157.3},
+           "cpu_baseline": cpu}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -374,6 +471,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--lmhead", action="store_true",
                     help="the fused LM head + commit line instead (an extra line, not the headline)")
+    ap.add_argument("--mamba", action="store_true",
+                    help="the denoiser's Mamba-2 scan + adaLN line instead (an extra line, not the headline)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -402,6 +501,9 @@ def main():
         w = dataclasses.replace(w, S=args.block_size, name=f"{w.name} (block size S={args.block_size})")
     if args.lmhead:
         lmhead_bench(args, torch, tt, TZ, W)
+        return
+    if args.mamba:
+        mamba_bench(args, torch, tt, TZ, W)
         return
     if w.layers != 1:
         loop_bench(w, args, torch, tt, TZ, W)

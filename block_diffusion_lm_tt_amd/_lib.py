@@ -34,6 +34,11 @@ class AttnShape(ctypes.Structure):
                 ("dtype", ctypes.c_int32)]
 
 
+class MambaShape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("S", ctypes.c_int32), ("H", ctypes.c_int32), ("P", ctypes.c_int32),
+                ("N", ctypes.c_int32), ("G", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
 class ProfileStats(ctypes.Structure):
     _fields_ = [("attn_calls", ctypes.c_int64), ("attn_total_ms", ctypes.c_double),
                 ("attn_main_ms", ctypes.c_double), ("commit_calls", ctypes.c_int64),
@@ -84,6 +89,12 @@ def lib() -> ctypes.CDLL:
         L.tt_lmhead_commit_workspace.argtypes = [i32, i32, i32, i32]
         L.tt_lmhead_commit.restype = i32
         L.tt_lmhead_commit.argtypes = [i32, i32, i32, i32, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp]
+        L.tt_mamba2_seeded_scan.restype = i32
+        L.tt_mamba2_seeded_scan.argtypes = [ctypes.POINTER(MambaShape)] + [vp] * 10 + [vp]
+        L.tt_adaln_modulate.restype = i32
+        L.tt_adaln_modulate.argtypes = [i32] * 4 + [vp] * 3 + [ctypes.c_float, vp, vp]
+        L.tt_adaln_gate.restype = i32
+        L.tt_adaln_gate.argtypes = [i32] * 4 + [vp] * 5 + [vp]
         L.tt_profile_enable.restype = i32
         L.tt_profile_enable.argtypes = [i32]
         L.tt_profile_reset.restype = i32
@@ -305,6 +316,87 @@ def tt_ctx_append(k_new, v_new, k_ctx, v_ctx, ctx_len, bump: bool = True, skippe
                              _stream(k_new.device, stream))
     _check("tt_ctx_append", st)
     return skipped
+
+
+def tt_mamba2_seeded_scan(x, dt, dt_bias, A_log, Dskip, Bm, Cm, h0, G: int, y=None, h_out=None,
+                          want_state: bool = False, stream=None):
+    """The denoiser's Mamba-2 scan over one block from the seeded state h0 (see include/tt.h).
+    x [B,S,H,P] and Bm, Cm [B,S,G,N] bf16 or fp32; dt [B,S,H], dt_bias/A_log/Dskip [H], h0
+    [B,H,P,N] fp32. Returns (y [B,S,H,P] in x's dtype, h_out fp32 [B,H,P,N] or None)."""
+    torch = _torch()
+    for name, t in (("x", x), ("dt", dt), ("dt_bias", dt_bias), ("A_log", A_log), ("Dskip", Dskip),
+                    ("Bm", Bm), ("Cm", Cm), ("h0", h0)):
+        _dev(t, name)
+    B, S, H, P = x.shape
+    N = Bm.shape[-1]
+    if Bm.shape != (B, S, G, N) or Cm.shape != Bm.shape:
+        raise ValueError("Bm/Cm must be [B,S,G,N]")
+    if dt.shape != (B, S, H) or h0.shape != (B, H, P, N):
+        raise ValueError("dt must be [B,S,H] and h0 [B,H,P,N]")
+    for name, t in (("dt_bias", dt_bias), ("A_log", A_log), ("Dskip", Dskip)):
+        if t.shape != (H,):
+            raise ValueError(f"{name} must be [H]")
+    for t in (dt, dt_bias, A_log, Dskip, h0):
+        if t.dtype != torch.float32:
+            raise TypeError("dt, dt_bias, A_log, Dskip and h0 must be float32")
+    dt_code = _dtype_code(x)
+    if Bm.dtype != x.dtype or Cm.dtype != x.dtype:
+        raise TypeError("x, Bm and Cm must share one dtype")
+    if y is None:
+        y = torch.empty_like(x)
+    _dev(y, "y")
+    if h_out is None and want_state:
+        h_out = torch.empty_like(h0)
+    if h_out is not None:
+        _dev(h_out, "h_out")
+    sh = MambaShape(B, S, H, P, N, G, dt_code)
+    st = lib().tt_mamba2_seeded_scan(ctypes.byref(sh), x.data_ptr(), dt.data_ptr(), dt_bias.data_ptr(),
+                                     A_log.data_ptr(), Dskip.data_ptr(), Bm.data_ptr(), Cm.data_ptr(),
+                                     h0.data_ptr(), y.data_ptr(), h_out.data_ptr() if h_out is not None else None,
+                                     _stream(x.device, stream))
+    _check("tt_mamba2_seeded_scan", st)
+    return y, h_out
+
+
+def _adaln_common(x, t_mod, table):
+    torch = _torch()
+    for name, t in (("x", x), ("t_mod", t_mod), ("table", table)):
+        _dev(t, name)
+    B, S, d = x.shape
+    if t_mod.shape != (B, 3, d) or table.shape != (3, d):
+        raise ValueError("t_mod must be [B,3,d] and table [3,d]")
+    if t_mod.dtype != torch.float32 or table.dtype != torch.float32:
+        raise TypeError("t_mod and table must be float32")
+    return B, S, d, _dtype_code(x)
+
+
+def tt_adaln_modulate(x, t_mod, table, eps: float = 1e-6, y=None, stream=None):
+    """y = LN(x) * (1 + scale) + shift with adaLN-single vectors (see include/tt.h)."""
+    torch = _torch()
+    B, S, d, dt = _adaln_common(x, t_mod, table)
+    if y is None:
+        y = torch.empty_like(x)
+    _dev(y, "y")
+    st = lib().tt_adaln_modulate(B, S, d, dt, x.data_ptr(), t_mod.data_ptr(), table.data_ptr(), float(eps),
+                                 y.data_ptr(), _stream(x.device, stream))
+    _check("tt_adaln_modulate", st)
+    return y
+
+
+def tt_adaln_gate(x, f, t_mod, table, out=None, stream=None):
+    """out = x + gate * f with adaLN-single vectors (see include/tt.h)."""
+    torch = _torch()
+    B, S, d, dt = _adaln_common(x, t_mod, table)
+    _dev(f, "f")
+    if f.shape != x.shape or f.dtype != x.dtype:
+        raise ValueError("f must match x")
+    if out is None:
+        out = torch.empty_like(x)
+    _dev(out, "out")
+    st = lib().tt_adaln_gate(B, S, d, dt, x.data_ptr(), f.data_ptr(), t_mod.data_ptr(), table.data_ptr(),
+                             out.data_ptr(), _stream(x.device, stream))
+    _check("tt_adaln_gate", st)
+    return out
 
 
 def profile_enable(on: bool = True):

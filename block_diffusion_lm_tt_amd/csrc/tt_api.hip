@@ -389,6 +389,83 @@ tt_status tt_ctx_append(const tt_attn_shape* shape, const void* k_new, const voi
   return launch_ctx_append(a, stream) == hipSuccess ? TT_OK : TT_ERR_HIP;
 }
 
+tt_status tt_mamba2_seeded_scan(const tt_mamba_shape* shape, const void* x, const float* dt,
+                                const float* dt_bias, const float* A_log, const float* Dskip,
+                                const void* Bm, const void* Cm, const float* h0, void* y, float* h_out,
+                                hipStream_t stream) {
+  if (!shape) return TT_ERR_INVALID_ARG;
+  const tt_mamba_shape& sh = *shape;
+  if (sh.B < 0 || sh.S < 1 || sh.H < 1 || sh.P < 1 || sh.N < 1 || sh.G < 1 || sh.H % sh.G != 0)
+    return TT_ERR_INVALID_ARG;
+  if (sh.dtype != TT_F32 && sh.dtype != TT_BF16) return TT_ERR_UNSUPPORTED;
+  if (!mamba_shape_supported(sh.P, sh.N) || sh.S > 1024) return TT_ERR_UNSUPPORTED;
+  if ((long long)sh.B * sh.H > kMaxGridBlocks) return TT_ERR_UNSUPPORTED;
+  if ((long long)sh.B * sh.S * sh.H * sh.P >= (1LL << 31) || (long long)sh.B * sh.H * sh.P * sh.N >= (1LL << 31) ||
+      (long long)sh.B * sh.S * sh.G * sh.N >= (1LL << 31))
+    return TT_ERR_UNSUPPORTED;
+  if (sh.B == 0) return TT_OK;
+  if (!x || !dt || !dt_bias || !A_log || !Dskip || !Bm || !Cm || !h0 || !y) return TT_ERR_INVALID_ARG;
+  if (((uintptr_t)h0 | (uintptr_t)h_out) % 16 != 0) return TT_ERR_UNSUPPORTED;  // 16-byte state loads
+  MambaArgs a;
+  a.x = x;
+  a.dt = dt;
+  a.dt_bias = dt_bias;
+  a.A_log = A_log;
+  a.Dskip = Dskip;
+  a.Bm = Bm;
+  a.Cm = Cm;
+  a.h0 = h0;
+  a.y = y;
+  a.h_out = h_out;
+  a.B = sh.B;
+  a.S = sh.S;
+  a.H = sh.H;
+  a.P = sh.P;
+  a.N = sh.N;
+  a.G = sh.G;
+  return launch_mamba2_scan(a, sh.dtype, stream) == hipSuccess ? TT_OK : TT_ERR_HIP;
+}
+
+static tt_status adaln_args(int32_t B, int32_t S, int32_t d, int32_t dtype, const void* x, const float* t_mod,
+                            const float* table, void* y, AdalnArgs* a) {
+  if (B < 0 || S < 1 || d < 1) return TT_ERR_INVALID_ARG;
+  if (dtype != TT_F32 && dtype != TT_BF16) return TT_ERR_UNSUPPORTED;
+  if (d > kAdalnMaxD || (long long)B * S > kMaxGridBlocks || (long long)B * S * d >= (1LL << 31))
+    return TT_ERR_UNSUPPORTED;
+  if (B == 0) return TT_OK;
+  if (!x || !t_mod || !table || !y) return TT_ERR_INVALID_ARG;
+  a->x = x;
+  a->f = nullptr;
+  a->t_mod = t_mod;
+  a->table = table;
+  a->y = y;
+  a->B = B;
+  a->S = S;
+  a->d = d;
+  a->eps = 0.0f;
+  return TT_OK;
+}
+
+tt_status tt_adaln_modulate(int32_t B, int32_t S, int32_t d, int32_t dtype, const void* x, const float* t_mod,
+                            const float* table, float eps, void* y, hipStream_t stream) {
+  AdalnArgs a;
+  if (!(eps >= 0.0f) || isinf(eps)) return TT_ERR_INVALID_ARG;
+  const tt_status st = adaln_args(B, S, d, dtype, x, t_mod, table, y, &a);
+  if (st != TT_OK || B == 0) return st;
+  a.eps = eps;
+  return launch_adaln_modulate(a, dtype, stream) == hipSuccess ? TT_OK : TT_ERR_HIP;
+}
+
+tt_status tt_adaln_gate(int32_t B, int32_t S, int32_t d, int32_t dtype, const void* x, const void* f,
+                        const float* t_mod, const float* table, void* out, hipStream_t stream) {
+  AdalnArgs a;
+  const tt_status st = adaln_args(B, S, d, dtype, x, t_mod, table, out, &a);
+  if (st != TT_OK || B == 0) return st;
+  if (!f) return TT_ERR_INVALID_ARG;
+  a.f = f;
+  return launch_adaln_gate(a, dtype, stream) == hipSuccess ? TT_OK : TT_ERR_HIP;
+}
+
 tt_status tt_profile_enable(int32_t enable) {
   std::lock_guard<std::mutex> lk(g_prof.mu);
   g_prof.enabled = enable != 0;

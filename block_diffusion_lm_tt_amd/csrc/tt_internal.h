@@ -128,4 +128,45 @@ struct LmHeadArgs {
 hipError_t launch_lmhead_reduce(const LmHeadArgs& a, hipStream_t s);
 hipError_t launch_lmhead_merge(const LmHeadArgs& a, hipStream_t s);
 
+// ---------------------------------------------------------------------------------------
+// the denoiser's Mamba-2 scan from the seeded state, and adaLN-single modulation
+// ---------------------------------------------------------------------------------------
+
+constexpr int kMambaChunk = 16;   // positions per chunk of the unrolled scan
+constexpr int kMambaMaxP = 128;   // head width
+constexpr int kMambaMaxN = 128;   // state width
+
+struct MambaArgs {
+  const void* x;         // [B,S,H,P] dtype
+  const float* dt;       // [B,S,H]
+  const float* dt_bias;  // [H]
+  const float* A_log;    // [H]
+  const float* Dskip;    // [H]
+  const void* Bm;        // [B,S,G,N] dtype
+  const void* Cm;        // [B,S,G,N] dtype
+  const float* h0;       // [B,H,P,N] the seeded state
+  void* y;               // [B,S,H,P] dtype
+  float* h_out;          // [B,H,P,N] or null
+  int B, S, H, P, N, G;
+};
+
+// P a power of 2 in [4, 128], N <= 128, N / (256 / P) in {4, 8, 16, 32, 64}
+bool mamba_shape_supported(int P, int N);
+hipError_t launch_mamba2_scan(const MambaArgs& a, int dtype, hipStream_t s);
+
+constexpr int kAdalnMaxD = 8192;  // row width of the modulation (32 elements per thread)
+
+struct AdalnArgs {
+  const void* x;         // [B,S,d] dtype
+  const void* f;         // [B,S,d] dtype (gated residual only)
+  const float* t_mod;    // [B,3,d] shift, scale, gate per sequence
+  const float* table;    // [3,d] the layer's offsets
+  void* y;               // [B,S,d] dtype
+  int B, S, d;
+  float eps;
+};
+
+hipError_t launch_adaln_modulate(const AdalnArgs& a, int dtype, hipStream_t s);
+hipError_t launch_adaln_gate(const AdalnArgs& a, int dtype, hipStream_t s);
+
 }  // namespace tt

@@ -32,3 +32,18 @@ def lmhead_to_device(x: W.LmHeadInputs, device):
     import torch
     return (to_torch(x.hidden, W.BF16, device), to_torch(x.weight, W.BF16, device),
             torch.from_numpy(np.ascontiguousarray(x.mask)).to(device))
+
+
+def mamba_to_device(m: W.MambaInputs, device):
+    """(x, dt, dt_bias, A_log, Dskip, Bm, Cm, h0) on the device."""
+    import torch
+    f = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)  # noqa: E731
+    return (to_torch(m.x, m.dtype, device), f(m.dt), f(m.dt_bias), f(m.A_log), f(m.Dskip),
+            to_torch(m.Bm, m.dtype, device), to_torch(m.Cm, m.dtype, device), f(m.h0))
+
+
+def adaln_to_device(a: W.AdalnInputs, device):
+    """(x, f, t_mod, table) on the device."""
+    import torch
+    f32 = lambda t: torch.from_numpy(np.ascontiguousarray(t, dtype=np.float32)).to(device)  # noqa: E731
+    return to_torch(a.x, a.dtype, device), to_torch(a.f, a.dtype, device), f32(a.t_mod), f32(a.table)

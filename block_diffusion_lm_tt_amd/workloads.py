@@ -34,7 +34,8 @@ F32 = "f32"
 BF16 = "bf16"
 
 # tensor ids for the per-tensor random streams
-_T_Q, _T_KB, _T_VB, _T_KC, _T_VC, _T_LEN, _T_LOGIT, _T_MASK, _T_PEAK, _T_BIAS, _T_HID, _T_HEAD = range(12)
+(_T_Q, _T_KB, _T_VB, _T_KC, _T_VC, _T_LEN, _T_LOGIT, _T_MASK, _T_PEAK, _T_BIAS, _T_HID, _T_HEAD, _T_MX, _T_MDT,
+ _T_MPAR, _T_MB, _T_MC, _T_MH0, _T_AX, _T_AF, _T_AT) = range(21)
 
 BF16_NAN = np.uint16(0x7FC0)
 
@@ -154,6 +155,69 @@ def make_lmhead(B: int, S: int, K: int, V: int, seed: int = 0, step: int = 0, ga
         mask = np.ones((B, S), dtype=np.uint8)
     return LmHeadInputs(B, S, K, V, f32_to_bf16_bits(h), w, np.ascontiguousarray(mask, dtype=np.uint8),
                         float(np.float32(gamma)))
+
+
+@dataclasses.dataclass
+class MambaInputs:
+    B: int
+    S: int
+    H: int
+    P: int
+    N: int
+    G: int
+    dtype: str
+    x: np.ndarray        # [B,S,H,P] dtype
+    dt: np.ndarray       # [B,S,H] fp32 (before the softplus)
+    dt_bias: np.ndarray  # [H] fp32
+    A_log: np.ndarray    # [H] fp32
+    Dskip: np.ndarray    # [H] fp32
+    Bm: np.ndarray       # [B,S,G,N] dtype
+    Cm: np.ndarray       # [B,S,G,N] dtype
+    h0: np.ndarray       # [B,H,P,N] fp32, the seeded state
+
+
+def make_mamba(B: int, S: int, H: int, P: int, N: int, G: int, dtype: str = BF16, seed: int = 0,
+               step: int = 0, layer: int = 0) -> MambaInputs:
+    """Inputs of the denoiser's Mamba-2 scan from a seeded state: x ~ N(0,1) and B, C ~ N(0, 1/N)
+    (so that B . C has unit variance), dt ~ N(0, 0.5), step biases placing softplus(dt_bias)
+    log-uniformly in [1e-3, 1e-1], A_log = log U(1, 16), D ~ U(0.5, 1.5), and a seeded state
+    ~ N(0, 0.5^2) (the context tower's state for the layer)."""
+    x = _normal(_rng(seed, _T_MX, step, layer), (B, S, H, P))
+    dt = _normal(_rng(seed, _T_MDT, step, layer), (B, S, H), 0.5)
+    r = _rng(seed, _T_MPAR, 0, layer)
+    dt0 = np.exp(r.uniform(np.log(1e-3), np.log(1e-1), H))
+    dt_bias = np.log(np.expm1(dt0)).astype(np.float32)
+    A_log = np.log(r.uniform(1.0, 16.0, H)).astype(np.float32)
+    Dskip = r.uniform(0.5, 1.5, H).astype(np.float32)
+    Bm = _normal(_rng(seed, _T_MB, step, layer), (B, S, G, N), 1.0 / math.sqrt(N))
+    Cm = _normal(_rng(seed, _T_MC, step, layer), (B, S, G, N), 1.0 / math.sqrt(N))
+    h0 = _normal(_rng(seed, _T_MH0, 0, layer), (B, H, P, N), 0.5)
+    return MambaInputs(B, S, H, P, N, G, dtype, _encode(x, dtype), dt, dt_bias, A_log, Dskip, _encode(Bm, dtype),
+                       _encode(Cm, dtype), h0)
+
+
+@dataclasses.dataclass
+class AdalnInputs:
+    B: int
+    S: int
+    d: int
+    dtype: str
+    x: np.ndarray       # [B,S,d] dtype
+    f: np.ndarray       # [B,S,d] dtype (the mixer's output, for the gated residual)
+    t_mod: np.ndarray   # [B,3,d] fp32: shift, scale, gate of each sequence's timestep
+    table: np.ndarray   # [3,d] fp32: the layer's offsets
+
+
+def make_adaln(B: int, S: int, d: int, dtype: str = BF16, seed: int = 0, layer: int = 0) -> AdalnInputs:
+    """adaLN-single inputs: rows x ~ 0.2 + N(0, 1.5^2) (a nonzero mean for the normalization
+    to remove), mixer outputs f ~ N(0,1), per-sequence vectors t_mod ~ N(0, 0.5^2) and the
+    layer's offsets ~ N(0, 0.1^2)."""
+    x = _normal(_rng(seed, _T_AX, 0, layer), (B, S, d), 1.5) + np.float32(0.2)
+    f = _normal(_rng(seed, _T_AF, 0, layer), (B, S, d))
+    rt = _rng(seed, _T_AT, 0, layer)
+    t_mod = (rt.standard_normal((B, 3, d)) * 0.5).astype(np.float32)
+    table = (rt.standard_normal((3, d)) * 0.1).astype(np.float32)
+    return AdalnInputs(B, S, d, dtype, _encode(x, dtype), _encode(f, dtype), t_mod, table)
 
 
 def make_attn(B: int, S: int, Hq: int, Hkv: int, D: int, ctx_lens: Sequence[int] | np.ndarray,

@@ -2,7 +2,8 @@
  * libtt -- the hot path of one block-wise diffusion decoding step, for AMD Instinct MI355X
  * (gfx950): the denoiser's block attention over its own block KV plus the frozen context
  * tower's same-layer KV, the confidence-threshold (gamma) commit (on given logits, or fused
- * behind the LM head), and the context cache update once a block is committed.
+ * behind the LM head), the context cache update once a block is committed, and the
+ * denoiser's Mamba-2 scan from the seeded state and adaLN-single time modulation.
  *
  * Method source: "Nemotron-TwoTower: Diffusion Language Modeling with Pretrained
  * Autoregressive Context" (gist.science explainer, English), Technical Summary; and the
@@ -229,6 +230,82 @@ tt_status tt_lmhead_commit(int32_t B, int32_t S, int32_t K, int32_t V, const voi
 tt_status tt_ctx_append(const tt_attn_shape *shape, const void *k_new, const void *v_new,
                         void *k_ctx, void *v_ctx, int32_t *ctx_len, int32_t bump,
                         uint8_t *skipped, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * tt_mamba2_seeded_scan -- the denoiser's Mamba-2 layer over one block, from the state the
+ * context tower hands over.
+ *
+ * Defined by the snilld.dk TwoTower article, "Hvad TwoTower aendrer teknisk" (the denoiser's
+ * Mamba-2 states are seeded directly from the context tower) and Nemotron-TwoTower
+ * (gist.science explainer), Technical Summary > Methodology > Architecture (the context
+ * tower produces layer-aligned KV caches and Mamba states) and its ablations (Mamba stays
+ * causal). Per sequence b and head h (group g = h / (H/G)), the Mamba-2 selective
+ * state-space recurrence over t = 0..S-1 from state_{-1} = h0[b,h]:
+ *
+ *   delta_t = softplus(dt[b,t,h] + dt_bias[h]),   a_t = exp(-exp(A_log[h]) delta_t)
+ *   state_t = a_t state_{t-1} + delta_t x[b,t,h,:] B[b,t,g,:]^T     (P x N)
+ *   y[b,t,h,:] = state_t C[b,t,g,:] + Dskip[h] x[b,t,h,:]
+ *
+ * and, when h_out is given, h_out[b,h] = state_{S-1} (the context tower's own state update
+ * over a committed block is the same call). fp32 arithmetic; y in the input dtype (bf16
+ * rounded to nearest even).
+ *
+ *   x        [B, S, H, P]  dtype       (device, read)
+ *   dt       [B, S, H]     float       (device, read), before the softplus
+ *   dt_bias, A_log, Dskip [H] float    (device, read)
+ *   Bm, Cm   [B, S, G, N]  dtype       (device, read)
+ *   h0       [B, H, P, N]  float       (device, read; 16-byte aligned)
+ *   y        [B, S, H, P]  dtype       (device, written)
+ *   h_out    [B, H, P, N]  float, may be NULL (device, written; 16-byte aligned)
+ *
+ * Supported: dtype TT_BF16 or TT_F32; P a power of 2 in [4, 128]; N <= 128 with N/(256/P)
+ * in {4, 8, 16, 32, 64} (e.g. P = 64, N = 128); S <= 1024; element counts < 2^31. Anything
+ * else returns TT_ERR_UNSUPPORTED (an h0/h_out off a 16-byte boundary too). B == 0 is a
+ * no-op. No workspace. h_out must not overlap h0.
+ * ------------------------------------------------------------------------------------- */
+typedef struct {
+    int32_t B, S, H, P, N, G;
+    int32_t dtype; /* tt_dtype of x, Bm, Cm and y */
+} tt_mamba_shape;
+
+tt_status tt_mamba2_seeded_scan(const tt_mamba_shape *shape, const void *x, const float *dt,
+                                const float *dt_bias, const float *A_log, const float *Dskip,
+                                const void *Bm, const void *Cm, const float *h0, void *y,
+                                float *h_out, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * tt_adaln_modulate / tt_adaln_gate -- adaLN-single time modulation of one denoiser layer.
+ *
+ * Defined by Nemotron-TwoTower (gist.science explainer), Technical Summary > Training and
+ * Conditioning > Time Conditioning (the denoiser is conditioned on the diffusion timestep
+ * through adaptive layer normalization) and the snilld.dk TwoTower article, "Hvad TwoTower
+ * aendrer teknisk" (every layer is time-modulated by a small adaLN-single block). The single
+ * block gives each sequence one set of vectors t_mod[b] = (shift, scale, gate) from its
+ * timestep, shared by all layers; each layer adds its own offsets table = (shift, scale,
+ * gate). For every row x[b,i,0:d]:
+ *
+ *   tt_adaln_modulate:  y = (x - mean) / sqrt(var + eps) * (1 + scale) + shift
+ *                       (mean and var of the row; no affine terms), before the mixer
+ *   tt_adaln_gate:      out = x + gate * f   (the mixer's output f joins the residual)
+ *
+ * with shift/scale/gate = t_mod[b, 0/1/2, :] + table[0/1/2, :]. fp32 arithmetic; outputs in
+ * the input dtype.
+ *
+ *   x, f, y, out  [B, S, d]  dtype   (device)
+ *   t_mod         [B, 3, d]  float   (device, read)
+ *   table         [3, d]     float   (device, read)
+ *   eps           finite, >= 0
+ *
+ * Supported: dtype TT_BF16 or TT_F32; d <= 8192; B*S*d < 2^31. Anything else returns
+ * TT_ERR_UNSUPPORTED. B == 0 is a no-op. y/out may be x itself (in place); no workspace.
+ * ------------------------------------------------------------------------------------- */
+tt_status tt_adaln_modulate(int32_t B, int32_t S, int32_t d, int32_t dtype, const void *x,
+                            const float *t_mod, const float *table, float eps, void *y,
+                            hipStream_t stream);
+
+tt_status tt_adaln_gate(int32_t B, int32_t S, int32_t d, int32_t dtype, const void *x,
+                        const void *f, const float *t_mod, const float *table, void *out,
+                        hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------
  * Kernel timing (measurement support). While enabled, each call records HIP events on its

@@ -61,6 +61,7 @@ def test_attn_workspace_query():
 
 
 FAKE = 0x1000  # never dereferenced: every call below fails validation before any launch
+FAKE16 = FAKE  # (16-byte aligned, for the alignment checks)
 
 
 @pytest.mark.parametrize("kw,want", [
@@ -187,3 +188,58 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 1, 1, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         tt.tt_block_denoise_attn(q, q, q, q, q, torch.zeros(1, dtype=torch.int32))
+
+
+def _mshape(**kw):
+    d = dict(B=32, S=16, H=128, P=64, N=128, G=8, dtype=_lib.TT_BF16)
+    d.update(kw)
+    return _lib.MambaShape(d["B"], d["S"], d["H"], d["P"], d["N"], d["G"], d["dtype"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(B=-1), INVALID), (dict(S=0), INVALID), (dict(H=0), INVALID), (dict(G=3), INVALID),
+    (dict(N=0), INVALID), (dict(dtype=7), UNSUPPORTED), (dict(P=4, N=16), UNSUPPORTED),
+    (dict(P=48), UNSUPPORTED), (dict(P=256), UNSUPPORTED), (dict(N=256), UNSUPPORTED), (dict(N=100), UNSUPPORTED),
+    (dict(S=1025), UNSUPPORTED), (dict(B=65536, H=256, G=8), UNSUPPORTED),
+])
+def test_mamba_scan_rejects_bad_shapes(kw, want):
+    L = tt.lib()
+    assert L.tt_mamba2_seeded_scan(ctypes.byref(_mshape(**kw)), *([FAKE16] * 10), None) == want
+
+
+def test_mamba_scan_null_pointers_alignment_and_empty_batch():
+    L = tt.lib()
+    sh = _mshape()
+    assert L.tt_mamba2_seeded_scan(None, *([FAKE16] * 10), None) == INVALID
+    for k in range(9):  # every argument but h_out is required
+        ptrs = [FAKE16] * 10
+        ptrs[k] = None
+        assert L.tt_mamba2_seeded_scan(ctypes.byref(sh), *ptrs, None) == INVALID
+    ptrs = [FAKE16] * 10
+    ptrs[7] = FAKE16 + 4  # h0 not 16-byte aligned
+    assert L.tt_mamba2_seeded_scan(ctypes.byref(sh), *ptrs, None) == UNSUPPORTED
+    ptrs = [FAKE16] * 10
+    ptrs[9] = FAKE16 + 8  # h_out not 16-byte aligned
+    assert L.tt_mamba2_seeded_scan(ctypes.byref(sh), *ptrs, None) == UNSUPPORTED
+    assert L.tt_mamba2_seeded_scan(ctypes.byref(_mshape(B=0)), *([None] * 10), None) == 0
+
+
+def test_adaln_validation():
+    L = tt.lib()
+    bf = _lib.TT_BF16
+    assert L.tt_adaln_modulate(2, 3, 0, bf, FAKE16, FAKE16, FAKE16, 1e-6, FAKE16, None) == INVALID
+    assert L.tt_adaln_modulate(-1, 3, 8, bf, FAKE16, FAKE16, FAKE16, 1e-6, FAKE16, None) == INVALID
+    assert L.tt_adaln_modulate(2, 0, 8, bf, FAKE16, FAKE16, FAKE16, 1e-6, FAKE16, None) == INVALID
+    assert L.tt_adaln_modulate(2, 3, 8, bf, FAKE16, FAKE16, FAKE16, -1.0, FAKE16, None) == INVALID
+    assert L.tt_adaln_modulate(2, 3, 8, bf, FAKE16, FAKE16, FAKE16, float("nan"), FAKE16, None) == INVALID
+    assert L.tt_adaln_modulate(2, 3, 8, bf, FAKE16, FAKE16, FAKE16, float("inf"), FAKE16, None) == INVALID
+    assert L.tt_adaln_modulate(2, 3, 8193, bf, FAKE16, FAKE16, FAKE16, 1e-6, FAKE16, None) == UNSUPPORTED
+    assert L.tt_adaln_modulate(2, 3, 8, 9, FAKE16, FAKE16, FAKE16, 1e-6, FAKE16, None) == UNSUPPORTED
+    for k in range(4):
+        ptrs = [FAKE16] * 4
+        ptrs[k] = None
+        assert L.tt_adaln_modulate(2, 3, 8, bf, *ptrs[:3], 1e-6, ptrs[3], None) == INVALID
+    assert L.tt_adaln_modulate(0, 3, 8, bf, None, None, None, 1e-6, None, None) == 0
+    assert L.tt_adaln_gate(2, 3, 8, bf, FAKE16, None, FAKE16, FAKE16, FAKE16, None) == INVALID
+    assert L.tt_adaln_gate(2, 3, 8193, bf, *([FAKE16] * 5), None) == UNSUPPORTED
+    assert L.tt_adaln_gate(0, 3, 8, bf, *([None] * 5), None) == 0

@@ -1,0 +1,190 @@
+"""GPU parity of the denoiser's Mamba-2 scan from the seeded state and of the adaLN-single
+modulation (through the C-ABI) against the fp64 oracle.
+
+Bars, from the arithmetic (fp32 evaluation, outputs in the input dtype):
+  * scan output y: |y - y_ref| <= r |y_ref| + 2^-15 T, where T bounds the sum of the terms'
+    magnitudes (sum_n |h0 C_t| + sum_{s<=t} delta_s |x_s| sum_n |C_t B_s| + |D x_t|; decays
+    <= 1), covering the fp32 sums (at most N + S terms, each rounding at 2^-24) and the
+    exp / softplus evaluations; r = 2^-8 for bf16 outputs (rounding to nearest even is
+    2^-9), 2^-20 for fp32;
+  * the state after the block (fp32): |h - h_ref| <= 2^-15 (|h0| + sum_s delta_s |x_s B_s|);
+  * modulation: |y - y_ref| <= r |y_ref| + 1e-5 ((|u| + 1) |1 + scale| + |shift|) + 1e-6, with
+    u the normalised input and the row statistics in fp32 (at most 32 sequential terms per
+    thread, then a tree over 256 threads: the standardised error stays near 40 * 2^-24);
+  * gated residual: |out - out_ref| <= r |out_ref| + 2^-20 (|x| + |gate f|).
+"""
+import numpy as np
+import pytest
+import torch
+
+from block_diffusion_lm_tt_amd import tensors as TZ
+from block_diffusion_lm_tt_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_diffusion_lm_tt_amd as tt
+    tt.lib()
+    return torch.device("cuda:0")
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _f(a, dtype):
+    return W.bf16_bits_to_f32(a).astype(np.float64) if dtype == W.BF16 else np.asarray(a, np.float64)
+
+
+def _scan_bound(m: W.MambaInputs):
+    """T per output element and the state bound per state element (see the module docstring)."""
+    x, Bm, Cm = _f(m.x, m.dtype), _f(m.Bm, m.dtype), _f(m.Cm, m.dtype)
+    delta = np.logaddexp(0.0, m.dt.astype(np.float64) + m.dt_bias.astype(np.float64)[None, None, :])
+    g = np.arange(m.H) // (m.H // m.G)
+    Cg, Bg = np.abs(Cm[:, :, g]), np.abs(Bm[:, :, g])              # [B,S,H,N]
+    ax = np.abs(x)
+    T = np.einsum("bhpn,bshn->bshp", np.abs(m.h0.astype(np.float64)), Cg, optimize=True)
+    cb = np.einsum("bthn,bshn->bhts", Cg, Bg)                       # [B,H,t,s]
+    cb = cb * np.tril(np.ones((m.S, m.S)))[None, None]
+    T += np.einsum("bhts,bsh,bshp->bthp", cb, delta, ax, optimize=True)
+    T += np.abs(m.Dskip.astype(np.float64))[None, None, :, None] * ax
+    Hb = np.abs(m.h0.astype(np.float64)) + np.einsum("bsh,bshp,bshn->bhpn", delta, ax, Bg, optimize=True)
+    return T, Hb
+
+
+def _gpu_scan(m, dev, want_state=True):
+    import block_diffusion_lm_tt_amd as tt
+    args = TZ.mamba_to_device(m, dev)
+    y, h = tt.tt_mamba2_seeded_scan(*args, G=m.G, want_state=want_state)
+    torch.cuda.synchronize()
+    return y.double().cpu().numpy(), (h.double().cpu().numpy() if h is not None else None)
+
+
+def _check_scan(m, dev, what, want_state=True):
+    from oracle import ttref_mamba2_scan
+    y, h = _gpu_scan(m, dev, want_state)
+    yr, hr = ttref_mamba2_scan(m.B, m.S, m.H, m.P, m.N, m.G, m.dtype, m.x, m.dt, m.dt_bias, m.A_log, m.Dskip,
+                               m.Bm, m.Cm, m.h0)
+    T, Hb = _scan_bound(m)
+    r = 2.0 ** -8 if m.dtype == W.BF16 else 2.0 ** -20
+    assert np.isfinite(y).all()
+    ex = np.abs(y - yr) / (r * np.abs(yr) + 2.0 ** -15 * T)
+    _say(f"{what}: y max-abs err {np.abs(y - yr).max():.3e}, worst fraction of the bound {ex.max():.3f}")
+    assert ex.max() <= 1.0
+    if want_state:
+        eh = np.abs(h - hr) / (2.0 ** -15 * Hb)
+        _say(f"{what}: state max-abs err {np.abs(h - hr).max():.3e}, worst fraction of the bound {eh.max():.3f}")
+        assert eh.max() <= 1.0
+
+
+SCAN_CASES = [
+    # name, B, S, H, P, N, G, dtype
+    ("bf16-p64-n128", 2, 5, 4, 64, 128, 2, W.BF16),
+    ("f32-p64-n128", 2, 5, 4, 64, 128, 2, W.F32),
+    ("bf16-S1", 3, 1, 4, 64, 128, 4, W.BF16),
+    ("bf16-S16", 2, 16, 8, 64, 128, 2, W.BF16),
+    ("bf16-S37-three-chunks", 2, 37, 4, 64, 128, 1, W.BF16),
+    ("f32-p32-n64", 2, 20, 6, 32, 64, 3, W.F32),
+    ("bf16-p128-n128", 1, 9, 2, 128, 128, 1, W.BF16),
+    ("bf16-p16-n64", 2, 7, 8, 16, 64, 8, W.BF16),
+    ("f32-p8-n128", 1, 3, 2, 8, 128, 2, W.F32),
+    ("bf16-p32-n128", 2, 16, 4, 32, 128, 4, W.BF16),
+]
+
+
+@pytest.mark.parametrize("case", SCAN_CASES, ids=[c[0] for c in SCAN_CASES])
+def test_scan_matches_oracle(dev, case):
+    name, B, S, H, P, N, G, dtype = case
+    m = W.make_mamba(B, S, H, P, N, G, dtype, seed=len(name))
+    _check_scan(m, dev, name)
+
+
+def test_scan_without_state_output(dev):
+    m = W.make_mamba(2, 16, 8, 64, 128, 2, W.BF16, seed=41)
+    _check_scan(m, dev, "no state output", want_state=False)
+
+
+def test_scan_full_batched_serving_shape(dev):
+    # B=32 sequences, block S=16, d_model 4096 -> 128 heads of 64, state 128, 8 groups
+    m = W.make_mamba(32, 16, 128, 64, 128, 8, W.BF16, seed=1003)
+    _say("scan at B=32 S=16 H=128 P=64 N=128 G=8 bf16")
+    _check_scan(m, dev, "batched serving")
+
+
+def test_scan_composes_over_a_split_block(dev):
+    # the state after the first part, fed back as the seed, continues the scan (fp32 inputs)
+    import block_diffusion_lm_tt_amd as tt
+    m = W.make_mamba(2, 24, 4, 64, 128, 2, W.F32, seed=42)
+    x, dt, bias, Al, Dk, Bm, Cm, h0 = TZ.mamba_to_device(m, dev)
+    y, h = tt.tt_mamba2_seeded_scan(x, dt, bias, Al, Dk, Bm, Cm, h0, G=2, want_state=True)
+    k = 10
+    part = lambda t, a, b_: t[:, a:b_].contiguous()  # noqa: E731
+    y1, h1 = tt.tt_mamba2_seeded_scan(part(x, 0, k), part(dt, 0, k), bias, Al, Dk, part(Bm, 0, k), part(Cm, 0, k),
+                                      h0, G=2, want_state=True)
+    y2, h2 = tt.tt_mamba2_seeded_scan(part(x, k, 24), part(dt, k, 24), bias, Al, Dk, part(Bm, k, 24),
+                                      part(Cm, k, 24), h1, G=2, want_state=True)
+    torch.cuda.synchronize()
+    assert torch.allclose(torch.cat([y1, y2], 1), y, rtol=1e-4, atol=1e-4)
+    assert torch.allclose(h2, h, rtol=1e-4, atol=1e-4)
+
+
+def _check_modulate(a, dev, what, eps=1e-6, in_place=False):
+    import block_diffusion_lm_tt_amd as tt
+    from oracle import ttref_adaln_modulate
+    x, f, tm, tab = TZ.adaln_to_device(a, dev)
+    y = tt.tt_adaln_modulate(x, tm, tab, eps=eps, y=x if in_place else None)
+    torch.cuda.synchronize()
+    got = y.double().cpu().numpy()
+    want = ttref_adaln_modulate(a.B, a.S, a.d, a.dtype, a.x, a.t_mod, a.table, eps=eps)
+    xf = _f(a.x, a.dtype)
+    u = (xf - xf.mean(-1, keepdims=True)) / np.sqrt(xf.var(-1, keepdims=True) + eps)
+    scale = (a.t_mod[:, 1] + a.table[1])[:, None].astype(np.float64)
+    shift = (a.t_mod[:, 0] + a.table[0])[:, None].astype(np.float64)
+    r = 2.0 ** -8 if a.dtype == W.BF16 else 2.0 ** -20
+    bound = r * np.abs(want) + 1e-5 * ((np.abs(u) + 1.0) * np.abs(1 + scale) + np.abs(shift)) + 1e-6
+    ex = np.abs(got - want) / bound
+    _say(f"{what}: max-abs err {np.abs(got - want).max():.3e}, worst fraction of the bound {ex.max():.3f}")
+    assert np.isfinite(got).all() and ex.max() <= 1.0
+
+
+ADALN_CASES = [("bf16-d4096", 4, 16, 4096, W.BF16), ("f32-d4096", 2, 3, 4096, W.F32),
+               ("bf16-d40", 3, 5, 40, W.BF16), ("bf16-d8192-max", 2, 2, 8192, W.BF16), ("f32-d1", 2, 2, 1, W.F32),
+               ("f32-d257", 1, 3, 257, W.F32)]
+
+
+@pytest.mark.parametrize("case", ADALN_CASES, ids=[c[0] for c in ADALN_CASES])
+def test_adaln_modulate_matches_oracle(dev, case):
+    name, B, S, d, dtype = case
+    _check_modulate(W.make_adaln(B, S, d, dtype, seed=len(name)), dev, name)
+
+
+def test_adaln_modulate_in_place_and_eps(dev):
+    a = W.make_adaln(2, 4, 300, W.F32, seed=7)
+    _check_modulate(a, dev, "in place", in_place=True)
+    _check_modulate(a, dev, "eps 0.5", eps=0.5)
+
+
+def test_adaln_full_batched_serving_shape(dev):
+    _check_modulate(W.make_adaln(32, 16, 4096, W.BF16, seed=1003), dev, "B=32 S=16 d=4096")
+
+
+@pytest.mark.parametrize("dtype,d", [(W.BF16, 4096), (W.F32, 37), (W.BF16, 8192)])
+def test_adaln_gate_matches_oracle(dev, dtype, d):
+    import block_diffusion_lm_tt_amd as tt
+    from oracle import ttref_adaln_gate
+    a = W.make_adaln(3, 5, d, dtype, seed=d)
+    x, f, tm, tab = TZ.adaln_to_device(a, dev)
+    out = tt.tt_adaln_gate(x, f, tm, tab)
+    torch.cuda.synchronize()
+    got = out.double().cpu().numpy()
+    want = ttref_adaln_gate(a.B, a.S, a.d, a.dtype, a.x, a.f, a.t_mod, a.table)
+    gate = (a.t_mod[:, 2] + a.table[2])[:, None].astype(np.float64)
+    r = 2.0 ** -8 if dtype == W.BF16 else 2.0 ** -20
+    bound = r * np.abs(want) + 2.0 ** -20 * (np.abs(_f(a.x, dtype)) + np.abs(gate * _f(a.f, dtype))) + 1e-30
+    ex = np.abs(got - want) / bound
+    _say(f"gate {dtype} d={d}: max-abs err {np.abs(got - want).max():.3e}, worst fraction {ex.max():.3f}")
+    assert ex.max() <= 1.0
