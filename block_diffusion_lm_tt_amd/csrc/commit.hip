@@ -125,9 +125,9 @@ struct DecideSmem {
 // Decide sequence b from its rows' chunk records: tokens, confidences, the gamma rule with
 // the fallback, and the fp64 recheck of the rows inside a band (when a.logits is given).
 // Writes the outputs of the masked rows, and of the unmasked rows too when write_unmasked.
-template <typename T, int NTH>
+template <typename T, int NTH, int MAXP>
 __device__ void decide_sequence(const CommitArgs& a, int b, bool write_unmasked, DecideSmem& sh) {
-  constexpr int MAXP = 1024 / NTH;  // positions per thread (S <= 1024)
+  // MAXP: positions per thread (S <= NTH * MAXP)
   const int tid = threadIdx.x;
   const T* logits = static_cast<const T*>(a.logits);
   bool msk[MAXP];
@@ -136,11 +136,27 @@ __device__ void decide_sequence(const CommitArgs& a, int b, bool write_unmasked,
   int tk[MAXP], fl[MAXP], dec[MAXP];
   int any_c = 0, nflag = 0, nmask = 0;
   const bool exact = a.logits != nullptr;  // else: no logits to recompute from
+  // the mask bytes and the first eight chunk records of every position are loaded together
+  // (records of unmasked rows are read and ignored), so that one round trip serves both
+  uint8_t mraw[MAXP];
+  unsigned long long r0[MAXP][8], z0[MAXP][8];
+#pragma unroll
+  for (int p = 0; p < MAXP; ++p) {
+    const size_t row = (size_t)b * a.S + min(tid + p * NTH, a.S - 1);
+    mraw[p] = a.mask[row];
+    const unsigned long long* c = reinterpret_cast<const unsigned long long*>(a.chunks + row * a.n_chunks);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int k = min(j, a.n_chunks - 1);
+      r0[p][j] = c[2 * k];
+      z0[p][j] = c[2 * k + 1];
+    }
+  }
 #pragma unroll
   for (int p = 0; p < MAXP; ++p) {
     const int i = tid + p * NTH;
     const size_t row = (size_t)b * a.S + i;
-    msk[p] = i < a.S && a.mask[row];
+    msk[p] = i < a.S && mraw[p];
     mm[p] = -INFINITY;
     zz[p] = 1.0;
     tk[p] = -1;
@@ -165,8 +181,8 @@ __device__ void decide_sequence(const CommitArgs& a, int b, bool write_unmasked,
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int k = min(k0 + j, a.n_chunks - 1);
-        r[j] = c[2 * k];
-        zb[j] = c[2 * k + 1];
+        r[j] = k0 == 0 ? r0[p][j] : c[2 * k];
+        zb[j] = k0 == 0 ? z0[p][j] : c[2 * k + 1];
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -377,18 +393,25 @@ __global__ __launch_bounds__(NT) void commit_reduce_kernel(CommitArgs a) {
 
 // ---- step 2: per-sequence decision -----------------------------------------------------
 
-template <typename T>
-__global__ __launch_bounds__(512) void commit_decide_kernel(CommitArgs a) {
+// one workgroup per sequence: a single wave for blocks of up to 64 positions, else 512 threads
+template <typename T, int NTH, int MAXP>
+__global__ __launch_bounds__(NTH) void commit_decide_kernel(CommitArgs a) {
   __shared__ DecideSmem dsm;
-  decide_sequence<T, 512>(a, blockIdx.x, true, dsm);
+  decide_sequence<T, NTH, MAXP>(a, blockIdx.x, true, dsm);
 }
 
 }  // namespace
 
-hipError_t launch_commit_decide(const CommitArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(commit_decide_kernel<uint16_t>, dim3(a.B), dim3(512), 0, s, a);
+template <typename T>
+hipError_t launch_decide_t(const CommitArgs& a, hipStream_t s) {
+  if (a.S <= 64)
+    hipLaunchKernelGGL((commit_decide_kernel<T, 64, 1>), dim3(a.B), dim3(64), 0, s, a);
+  else
+    hipLaunchKernelGGL((commit_decide_kernel<T, 512, 2>), dim3(a.B), dim3(512), 0, s, a);
   return hipGetLastError();
 }
+
+hipError_t launch_commit_decide(const CommitArgs& a, hipStream_t s) { return launch_decide_t<uint16_t>(a, s); }
 
 int commit_chunk_elems(int dtype) { return NT * LOADS * (dtype == TT_BF16 ? 8 : 4); }
 
@@ -426,11 +449,7 @@ hipError_t launch_commit(const CommitArgs& a, hipStream_t s, hipEvent_t ev_reduc
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (ev_reduce_end) (void)hipEventRecord(ev_reduce_end, s);
-  if (a.dtype == TT_BF16)
-    hipLaunchKernelGGL(commit_decide_kernel<uint16_t>, dim3(a.B), dim3(512), 0, s, a);
-  else
-    hipLaunchKernelGGL(commit_decide_kernel<float>, dim3(a.B), dim3(512), 0, s, a);
-  return hipGetLastError();
+  return a.dtype == TT_BF16 ? launch_decide_t<uint16_t>(a, s) : launch_decide_t<float>(a, s);
 }
 
 }  // namespace tt
