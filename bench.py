@@ -214,20 +214,76 @@ def loop_bench(w, args, torch, tt, TZ, W):
     print(json.dumps(res), flush=True)
 
 
-def stream_read_ceiling(torch, dev) -> float:
-    """A streaming read measured in the same run: a library reduction over 2 GiB of fp32
-    (read once, a scalar written), best of five, in GB/s."""
-    x = torch.ones((1 << 29,), dtype=torch.float32, device=dev)
-    best = 0.0
-    for _ in range(6):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        x.sum()
-        e1.record()
-        torch.cuda.synchronize()
-        best = max(best, x.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9)
-    del x
-    return best
+def stream_read_ceiling(torch, dev) -> dict:
+    """Plain HBM streaming reads measured in the same run: the probe kernels of
+    block_diffusion_lm_tt_amd/libttprobe.so over 2 GiB -- 16-byte non-temporal loads into
+    registers, and 16-byte LDS-DMA copies -- for several grid sizes, best of four each. GB/s
+    is the better of the two; both are reported with their grid."""
+    import ctypes
+    from block_diffusion_lm_tt_amd.build import PROBE_LIB
+    L = ctypes.CDLL(PROBE_LIB)
+    for fn in (L.ttprobe_stream_read, L.ttprobe_stream_read_lds):
+        fn.restype = ctypes.c_int
+        fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    nbytes = 1 << 31
+    x = torch.ones((nbytes,), dtype=torch.uint8, device=dev)
+    sink = torch.empty((1 << 15,), dtype=torch.int32, device=dev)
+    st = torch.cuda.current_stream(dev)
+    out = {"bytes": nbytes}
+    for name, fn in (("registers", L.ttprobe_stream_read), ("lds_dma", L.ttprobe_stream_read_lds)):
+        best, best_grid = 0.0, 0
+        for blocks in (1024, 2048, 4096, 8192, 16384):
+            for _ in range(4):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                rc = fn(x.data_ptr(), nbytes, sink.data_ptr(), blocks, st.cuda_stream)
+                e1.record()
+                if rc != 0:
+                    raise RuntimeError(f"stream-read probe ({name}) failed: {rc}")
+                torch.cuda.synchronize()
+                gbs = nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9
+                if gbs > best:
+                    best, best_grid = gbs, blocks
+        out[name] = {"GBps": best, "workgroups": best_grid}
+    out["GBps"] = max(out["registers"]["GBps"], out["lds_dma"]["GBps"])
+    log(f"[bench] streaming read ceiling: registers {out['registers']['GBps']:.0f} GB/s "
+        f"({out['registers']['workgroups']} workgroups), LDS-DMA {out['lds_dma']['GBps']:.0f} GB/s "
+        f"({out['lds_dma']['workgroups']} workgroups)")
+    del x, sink
+    return out
+
+
+def stream_read_same_size(torch, dev, nbytes: int) -> dict:
+    """The register-streaming probe over exactly `nbytes` (four rotated buffers, so that the
+    last-level cache cannot serve them), best over grid sizes of the median of five
+    event-timed launches: the practical ceiling for a kernel that reads that many bytes once."""
+    import ctypes
+    from block_diffusion_lm_tt_amd.build import PROBE_LIB
+    L = ctypes.CDLL(PROBE_LIB)
+    L.ttprobe_stream_read.restype = ctypes.c_int
+    L.ttprobe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                      ctypes.c_void_p]
+    nb = (int(nbytes) + 255) // 256 * 256
+    R = 4
+    bufs = [torch.ones((nb,), dtype=torch.uint8, device=dev) for _ in range(R)]
+    sink = torch.empty((1 << 15,), dtype=torch.int32, device=dev)
+    st = torch.cuda.current_stream(dev)
+    best, grid = float("inf"), 0
+    for blocks in (256, 512, 1024, 2048, 4096, 8192):
+        ts = []
+        for k in range(6):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            if L.ttprobe_stream_read(bufs[k % R].data_ptr(), nb, sink.data_ptr(), blocks, st.cuda_stream) != 0:
+                raise RuntimeError("stream-read probe failed")
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        t = float(np.median(ts[1:]))
+        if t < best:
+            best, grid = t, blocks
+    del bufs, sink
+    return {"bytes": nb, "us": best * 1e6, "GBps": nb / best / 1e9, "workgroups": grid}
 
 
 def copy_probe(args, torch, dev):
@@ -421,6 +477,8 @@ def mamba_bench(args, torch, tt, TZ, W):
     flop = 2.0 * B * H * S * P * N  # the readout of the seeded state, the arithmetic bulk
     ad_mod = 2 * B * S * d * act + (B * 3 * d + 3 * d) * 4
     ad_gate = 3 * B * S * d * act + (B * 3 * d + 3 * d) * 4
+    stream = stream_read_ceiling(torch, dev)
+    same = stream_read_same_size(torch, dev, alg)
     log(f"[mamba] scan {t_scan*1e6:.1f} us/call (p10/p50/p90 {p10:.1f}/{p50:.1f}/{p90:.1f}; {gbs:.0f} GB/s), "
         f"with the state written {t_state*1e6:.1f} us; adaLN modulate {t_mod*1e6:.1f} us, gate {t_gate*1e6:.1f} us")
     cpu = None
@@ -452,7 +510,12 @@ def mamba_bench(args, torch, tt, TZ, W):
            "roofline": {"kernel": "mamba2_scan_kernel", "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
                         "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None, "avg_us": t_scan * 1e6,
                         "algorithmic_bytes_per_launch": alg, "fp32_flop_per_launch": flop,
-                        "fp32_frac": flop / t_scan / 1e12 / 157.3},
+                        "fp32_frac": flop / t_scan / 1e12 / 157.3,
+                        "frac_of_measured_stream_read": gbs / stream["GBps"],
+                        "frac_of_same_size_stream_read": same["us"] / (t_scan * 1e6)},
+           "hbm_stream_read_probe": stream, "stream_read_same_bytes": same,
+        "stream_read_same_bytes_as_context_kv": same,
+        "stream_read_same_bytes_as_commit": same_c,
            "cpu_baseline": cpu}
     print(json.dumps(res), flush=True)
 
@@ -573,7 +636,10 @@ def main():
     torch.cuda.synchronize()
     per_call = np.array([evs[k].elapsed_time(evs[k + 1]) * 1e3 for k in range(n_dist)])
     p10, p50, p90 = (float(np.percentile(per_call, p)) for p in (10, 50, 90))
-    stream_gbs = stream_read_ceiling(torch, dev)
+    stream = stream_read_ceiling(torch, dev)
+    stream_gbs = stream["GBps"]
+    same = stream_read_same_size(torch, dev, x.ctx_kv_bytes)
+    same_c = stream_read_same_size(torch, dev, c.masked_row_bytes)
 
     copy_probe(args, torch, dev)
 
@@ -617,6 +683,9 @@ def main():
         "context_kv_GBps": gbs_call,
         "context_kv_pct_hbm_peak": 100.0 * gbs_call / HBM_PEAK_GBS,
         "hbm_stream_read_GBps_measured": stream_gbs,
+        "hbm_stream_read_probe": stream,
+        "stream_read_same_bytes_as_context_kv": same,
+        "stream_read_same_bytes_as_commit": same_c,
         "context_kv_pct_of_measured_stream_read": 100.0 * gbs_call / stream_gbs,
         "attn_us_per_call": t_attn_plain * 1e6,
         "attn_us_per_call_p10_p50_p90": [p10, p50, p90],
@@ -630,6 +699,10 @@ def main():
                      "traffic": profiled_traffic("attn_mfma_kernel")
                      if args.config == 3 and not args.block_size else None,
                      "avg_us": t_main * 1e6, "algorithmic_bytes_per_launch": kv_bytes,
+                     "call_achieved": gbs_call, "call_frac": gbs_call / HBM_PEAK_GBS,
+                     "call_us": t_attn_plain * 1e6,
+                     "frac_of_measured_stream_read": gbs_main / stream_gbs,
+                     "frac_of_same_size_stream_read": same["us"] / (t_main * 1e6),
                      "profiled_avg_us": profiled_avg_us("attn_mfma_kernel")
                      if args.config == 3 and not args.block_size else None},
         "cpu_baseline": cpu,

@@ -11,6 +11,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtt.so")
+# a measurement probe (a plain streaming read, the benchmark's bandwidth ceiling), a library of
+# its own so that it is not part of libtt's interface
+PROBE_SRC = os.path.join(CSRC, "probe", "stream_read.hip")
+PROBE_LIB = os.path.join(HERE, "libttprobe.so")
 BUILD = os.path.join(ROOT, "_build", "libtt")
 ARCH = os.environ.get("TT_OFFLOAD_ARCH", "gfx950")
 
@@ -72,6 +76,14 @@ def build(verbose: bool = False) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [HIPCC, *FLAGS, "-shared", PROBE_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {PROBE_SRC}:\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 
