@@ -95,6 +95,12 @@ def lib() -> ctypes.CDLL:
         L.tt_adaln_modulate.argtypes = [i32] * 4 + [vp] * 3 + [ctypes.c_float, vp, vp]
         L.tt_adaln_gate.restype = i32
         L.tt_adaln_gate.argtypes = [i32] * 4 + [vp] * 5 + [vp]
+        L.tt_lmhead_commit_exact_workspace.restype = sz
+        L.tt_lmhead_commit_exact_workspace.argtypes = [i32] * 4
+        L.tt_lmhead_commit_exact.restype = i32
+        L.tt_lmhead_commit_exact.argtypes = [i32] * 4 + [vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp, sz, vp]
+        L.tt_lmhead_weight_bound.restype = i32
+        L.tt_lmhead_weight_bound.argtypes = [vp, i32, i32, vp, vp]
         L.tt_profile_enable.restype = i32
         L.tt_profile_enable.argtypes = [i32]
         L.tt_profile_reset.restype = i32
@@ -238,9 +244,11 @@ def tt_lmhead_commit_workspace(B, S, K, V) -> int:
 
 
 def tt_lmhead_commit(hidden, weight, mask, gamma: float, token_id=None, committed=None, conf=None,
-                     want_conf: bool = True, workspace=None, stream=None):
+                     want_conf: bool = True, workspace=None, stream=None, w_bound=None):
     """LM head + commit (see include/tt.h): hidden bf16 [B,S,K], weight bf16 [V,K], mask uint8
-    [B,S]. Returns (token_id int32[B,S], committed uint8[B,S], conf float32[B,S] or None)."""
+    [B,S]. With w_bound (a float32 device tensor of one element, from tt_lmhead_weight_bound)
+    the exact mode (tt_lmhead_commit_exact) runs. Returns (token_id int32[B,S], committed
+    uint8[B,S], conf float32[B,S] or None)."""
     torch = _torch()
     _dev(hidden, "hidden")
     _dev(weight, "weight")
@@ -270,16 +278,45 @@ def tt_lmhead_commit(hidden, weight, mask, gamma: float, token_id=None, committe
         if conf.dtype != torch.float32 or conf.shape != (B, S):
             raise ValueError("conf must be float32 [B,S]")
         _dev(conf, "conf")
-    need = tt_lmhead_commit_workspace(B, S, K, V)
+    if w_bound is not None:
+        _dev(w_bound, "w_bound")
+        if w_bound.dtype != torch.float32 or w_bound.numel() != 1:
+            raise ValueError("w_bound must be a float32 tensor of one element")
+        need = int(lib().tt_lmhead_commit_exact_workspace(B, S, K, V))
+    else:
+        need = tt_lmhead_commit_workspace(B, S, K, V)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     _dev(workspace, "workspace")
-    st = lib().tt_lmhead_commit(B, S, K, V, hidden.data_ptr(), weight.data_ptr(), mask.data_ptr(),
-                                float(gamma), token_id.data_ptr(), committed.data_ptr(),
-                                conf.data_ptr() if conf is not None else None, workspace.data_ptr(),
-                                workspace.numel(), _stream(dev, stream))
-    _check("tt_lmhead_commit", st)
+    cp = conf.data_ptr() if conf is not None else None
+    if w_bound is not None:
+        st = lib().tt_lmhead_commit_exact(B, S, K, V, hidden.data_ptr(), weight.data_ptr(), mask.data_ptr(),
+                                          float(gamma), w_bound.data_ptr(), token_id.data_ptr(),
+                                          committed.data_ptr(), cp, workspace.data_ptr(), workspace.numel(),
+                                          _stream(dev, stream))
+        _check("tt_lmhead_commit_exact", st)
+    else:
+        st = lib().tt_lmhead_commit(B, S, K, V, hidden.data_ptr(), weight.data_ptr(), mask.data_ptr(),
+                                    float(gamma), token_id.data_ptr(), committed.data_ptr(), cp,
+                                    workspace.data_ptr(), workspace.numel(), _stream(dev, stream))
+        _check("tt_lmhead_commit", st)
     return token_id, committed, conf
+
+
+def tt_lmhead_weight_bound(weight, bound=None, stream=None):
+    """An upper bound on max_v ||weight[v]||_2 (see include/tt.h), as a float32 device tensor of
+    one element: the w_bound of the exact LM head mode."""
+    torch = _torch()
+    _dev(weight, "weight")
+    if weight.dtype != torch.bfloat16 or weight.dim() != 2:
+        raise ValueError("weight must be bfloat16 [V,K]")
+    if bound is None:
+        bound = torch.empty((1,), dtype=torch.float32, device=weight.device)
+    _dev(bound, "bound")
+    V, K = weight.shape
+    st = lib().tt_lmhead_weight_bound(weight.data_ptr(), V, K, bound.data_ptr(), _stream(weight.device, stream))
+    _check("tt_lmhead_weight_bound", st)
+    return bound
 
 
 def tt_ctx_append(k_new, v_new, k_ctx, v_ctx, ctx_len, bump: bool = True, skipped=None,

@@ -82,16 +82,21 @@ __device__ __forceinline__ const char* uniform_ptr(const char* p) {
 
 // (m, tok, z) merge of two partials over disjoint vocabulary sets: larger max wins, equal
 // maxima keep the lower index; z moves to the common max. An empty partial has m = -inf.
-__device__ __forceinline__ void part_merge(float& m, int& tok, float& z, float m2, int tok2, float z2) {
+// The runner-up r (the largest value after the max, counting a repeated max) of a union of
+// two sets is the largest of the two runners-up and the smaller maximum.
+__device__ __forceinline__ void part_merge(float& m, int& tok, float& z, float& r, float m2, int tok2, float z2,
+                                           float r2) {
   if (m2 == -INFINITY) return;
   if (m == -INFINITY) {
     m = m2;
     tok = tok2;
     z = z2;
+    r = r2;
     return;
   }
   const float M = fmaxf(m, m2);
   z = z * exp2f((m - M) * kLog2e) + z2 * exp2f((m2 - M) * kLog2e);
+  r = fmaxf(fmaxf(r, r2), fminf(m, m2));
   if (m2 > m || (m2 == m && tok2 < tok)) tok = tok2;
   m = M;
 }
@@ -258,10 +263,11 @@ __global__ __launch_bounds__(NTHR, 1) void lmhead_reduce_kernel(LmHeadArgs a) {
   float* pm = reinterpret_cast<float*>(g_lds);
   int* pt = reinterpret_cast<int*>(g_lds + RT * 4 * 4);
   float* pz = reinterpret_cast<float*>(g_lds + RT * 4 * 8);
+  float* pr = reinterpret_cast<float*>(g_lds + RT * 4 * 12);
   const int v0 = vt * VT + wv * 64 + 4 * lh;
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    float m = -INFINITY;
+    float m = -INFINITY, rr = -INFINITY;  // max and runner-up
     int tok = 0x7fffffff;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -269,9 +275,14 @@ __global__ __launch_bounds__(NTHR, 1) void lmhead_reduce_kernel(LmHeadArgs a) {
       for (int i = 0; i < 16; ++i) {
         const int v = v0 + mb * 32 + 8 * (i >> 2) + (i & 3);
         const float x = acc[mb][nb][i];
-        if (v < a.V && x > m) {
-          m = x;
-          tok = v;
+        if (v < a.V) {
+          if (x > m) {
+            rr = m;
+            m = x;
+            tok = v;
+          } else {
+            rr = fmaxf(rr, x);
+          }
         }
       }
     // exp of (x - m): the difference first, so the max term is exactly 1 and each exponent's
@@ -289,17 +300,19 @@ __global__ __launch_bounds__(NTHR, 1) void lmhead_reduce_kernel(LmHeadArgs a) {
     const float m2 = __shfl_xor(m, 32);
     const int t2 = __shfl_xor(tok, 32);
     const float z2 = __shfl_xor(z, 32);
-    part_merge(m, tok, z, m2, t2, z2);
+    const float r2 = __shfl_xor(rr, 32);
+    part_merge(m, tok, z, rr, m2, t2, z2, r2);
     if (lh == 0) {
       const int r = wr * 64 + nb * 32 + lr;
       pm[r * 4 + wv] = m;
       pt[r * 4 + wv] = tok;
       pz[r * 4 + wv] = z;
+      pr[r * 4 + wv] = rr;
     }
   }
   __syncthreads();
   if (tid < nrows) {
-    float m = pm[tid * 4];
+    float m = pm[tid * 4], rr = pr[tid * 4];
     int tok = pt[tid * 4];
     double z = pz[tid * 4];
 #pragma unroll
@@ -307,14 +320,17 @@ __global__ __launch_bounds__(NTHR, 1) void lmhead_reduce_kernel(LmHeadArgs a) {
       const float m2 = pm[tid * 4 + w];
       if (m2 == -INFINITY) continue;
       const double z2 = pz[tid * 4 + w];
+      const float r2 = pr[tid * 4 + w];
       if (m == -INFINITY) {
         m = m2;
         tok = pt[tid * 4 + w];
         z = z2;
+        rr = r2;
         continue;
       }
       const float M = fmaxf(m, m2);
       z = z * exp((double)m - (double)M) + z2 * exp((double)m2 - (double)M);
+      rr = fmaxf(fmaxf(rr, r2), fminf(m, m2));
       if (m2 > m) tok = pt[tid * 4 + w];  // equal maxima keep the earlier (lower) block
       m = M;
     }
@@ -322,61 +338,92 @@ __global__ __launch_bounds__(NTHR, 1) void lmhead_reduce_kernel(LmHeadArgs a) {
     c.m = m;
     c.tok = tok;
     c.z = z;
-    a.chunks[(size_t)g_rows[tid] * a.NVT + vt] = c;
+    const size_t at = (size_t)g_rows[tid] * a.NVT + vt;
+    a.chunks[at] = c;
+    a.runner[at] = rr;
   }
 }
 
 // Merge of a masked row's NVT chunk records into one (the decide step then reads one record
 // per row): 256 threads, each merges its chunks (k = t, t + 256, ...) in fp64, then the
 // workgroup merges the threads' partials; larger max wins, equal maxima keep the lower index
-// (an order-free rule), z moves to the common max in fp64.
+// (an order-free rule), z moves to the common max in fp64. The row's runner-up logit is
+// merged alongside. In exact mode (a weight bound is given) the workgroup also bounds the
+// error of the row's fp32 logits: each is a sum of K exact bf16 products accumulated in fp32
+// in some order, so it lies within 2 K 2^-24 sum_k |h_k w_vk| (a factor 2 covers a rounding
+// that is not to nearest) <= 2 K 2^-24 ||h||_2 max_v ||w_v||_2 of the exact value.
 constexpr int MT = 256;
 
-__device__ __forceinline__ void merge_d(float& m, int& tok, double& z, float m2, int tok2, double z2) {
+__device__ __forceinline__ void merge_d(float& m, int& tok, double& z, float& r, float m2, int tok2, double z2,
+                                        float r2) {
   if (m2 == -INFINITY) return;
   if (m == -INFINITY) {
     m = m2;
     tok = tok2;
     z = z2;
+    r = r2;
     return;
   }
   const float M = fmaxf(m, m2);
   z = z * exp((double)m - (double)M) + z2 * exp((double)m2 - (double)M);
+  r = fmaxf(fmaxf(r, r2), fminf(m, m2));
   if (m2 > m || (m2 == m && tok2 < tok)) tok = tok2;
   m = M;
 }
 
 __global__ __launch_bounds__(MT) void lmhead_merge_kernel(LmHeadArgs a) {
-  __shared__ float sm[MT / 64];
+  __shared__ float sm[MT / 64], sr[MT / 64];
   __shared__ int st[MT / 64];
-  __shared__ double sz[MT / 64];
+  __shared__ double sz[MT / 64], sh[MT / 64];
   const int row = blockIdx.x, tid = threadIdx.x;
+  if (row == 0 && tid == 0 && a.count) *a.count = 0;  // the flag step's counter
   if (!a.mask[row]) return;
   const CommitChunk* c = a.chunks + (size_t)row * a.NVT;
-  float m = -INFINITY;
+  const float* rc = a.runner + (size_t)row * a.NVT;
+  float m = -INFINITY, r = -INFINITY;
   int tok = 0x7fffffff;
   double z = 0.0;
-  for (int k = tid; k < a.NVT; k += MT) merge_d(m, tok, z, c[k].m, c[k].tok, c[k].z);
+  for (int k = tid; k < a.NVT; k += MT) merge_d(m, tok, z, r, c[k].m, c[k].tok, c[k].z, rc[k]);
+  // (exact mode) ||h||_2^2 of the row, in fp64 (each square of a bf16 value is exact)
+  double hh = 0.0;
+  if (a.w_bound) {
+    const uint16_t* h = static_cast<const uint16_t*>(a.hidden) + (size_t)row * a.K;
+    for (int k = tid; k < a.K; k += MT) {
+      const double x = (double)__uint_as_float(((uint32_t)h[k]) << 16);
+      hh = fma(x, x, hh);
+    }
+  }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
     const float m2 = __shfl_xor(m, off);
     const int t2 = __shfl_xor(tok, off);
     const double z2 = __shfl_xor(z, off);
-    merge_d(m, tok, z, m2, t2, z2);
+    const float r2 = __shfl_xor(r, off);
+    merge_d(m, tok, z, r, m2, t2, z2, r2);
+    hh += __shfl_xor(hh, off);
   }
   if ((tid & 63) == 0) {
     sm[tid >> 6] = m;
     st[tid >> 6] = tok;
     sz[tid >> 6] = z;
+    sr[tid >> 6] = r;
+    sh[tid >> 6] = hh;
   }
   __syncthreads();
   if (tid == 0) {
-    for (int w = 1; w < MT / 64; ++w) merge_d(m, tok, z, sm[w], st[w], sz[w]);
-    CommitChunk r;
-    r.m = m;
-    r.tok = tok;
-    r.z = z;
-    a.merged[row] = r;
+    for (int w = 1; w < MT / 64; ++w) merge_d(m, tok, z, r, sm[w], st[w], sz[w], sr[w]);
+    CommitChunk rec;
+    rec.m = m;
+    rec.tok = tok;
+    rec.z = z;
+    a.merged[row] = rec;
+    if (a.w_bound) {
+      const double hn = sqrt((sh[0] + sh[1]) + (sh[2] + sh[3]));
+      // the bound's own rounding (a few fp64 operations) is covered by the factor 1 + 1e-12
+      const double eps = 2.0 * (double)a.K * 0x1p-24 * hn * (double)*a.w_bound * (1.0 + 1e-12);
+      a.rowx[2 * (size_t)row] = (double)r;
+      a.rowx[2 * (size_t)row + 1] = eps;
+    }
   }
 }
 

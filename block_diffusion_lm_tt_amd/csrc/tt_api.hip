@@ -72,7 +72,13 @@ tt_status plan_commit(int32_t B, int32_t S, int32_t V, int32_t dtype, CommitPlan
 
 struct LmPlan {
   int NRG, NVT;
-  size_t chunk_bytes, merged_bytes;
+  size_t chunk_bytes, runner_bytes, merged_bytes;
+  // exact mode
+  size_t rowx_bytes, flags_bytes, list_bytes, count_bytes, state_bytes, need_bytes, exact_bytes;
+  size_t base() const { return chunk_bytes + runner_bytes + merged_bytes; }
+  size_t exact_total() const {
+    return base() + rowx_bytes + flags_bytes + list_bytes + count_bytes + state_bytes + need_bytes + exact_bytes;
+  }
 };
 
 tt_status plan_lmhead(int32_t B, int32_t S, int32_t K, int32_t V, LmPlan* p) {
@@ -82,8 +88,17 @@ tt_status plan_lmhead(int32_t B, int32_t S, int32_t K, int32_t V, LmPlan* p) {
   if ((long long)B * S * K >= (1LL << 31)) return TT_ERR_UNSUPPORTED;
   p->NRG = (B * S + kLmRowsPerWg - 1) / kLmRowsPerWg;
   p->NVT = (int)(((long long)V + kLmVocabPerWg - 1) / kLmVocabPerWg);
-  p->chunk_bytes = align_up((size_t)B * S * p->NVT * sizeof(CommitChunk));
-  p->merged_bytes = align_up((size_t)B * S * sizeof(CommitChunk));
+  const size_t rows = (size_t)B * S;
+  p->chunk_bytes = align_up(rows * p->NVT * sizeof(CommitChunk));
+  p->runner_bytes = align_up(rows * p->NVT * sizeof(float));
+  p->merged_bytes = align_up(rows * sizeof(CommitChunk));
+  p->rowx_bytes = align_up(rows * 2 * sizeof(double));
+  p->flags_bytes = align_up(rows * sizeof(int));
+  p->list_bytes = align_up(rows * sizeof(int));
+  p->count_bytes = align_up(sizeof(int));
+  p->state_bytes = align_up((size_t)B * sizeof(int));
+  p->need_bytes = align_up(rows * p->NVT);
+  p->exact_bytes = align_up(rows * p->NVT * sizeof(ExactChunk));
   return TT_OK;
 }
 
@@ -291,7 +306,7 @@ tt_status tt_commit_noalloc(int32_t B, int32_t S, int32_t V, int32_t dtype, cons
 size_t tt_lmhead_commit_workspace(int32_t B, int32_t S, int32_t K, int32_t V) {
   LmPlan p;
   if (plan_lmhead(B, S, K, V, &p) != TT_OK) return 0;
-  return p.chunk_bytes + p.merged_bytes;
+  return p.base();
 }
 
 tt_status tt_lmhead_commit(int32_t B, int32_t S, int32_t K, int32_t V, const void* hidden,
@@ -312,8 +327,13 @@ tt_status tt_lmhead_commit(int32_t B, int32_t S, int32_t K, int32_t V, const voi
   l.hidden = hidden;
   l.weight = weight;
   l.mask = mask;
-  l.chunks = static_cast<CommitChunk*>(workspace);
-  l.merged = reinterpret_cast<CommitChunk*>(static_cast<char*>(workspace) + p.chunk_bytes);
+  char* ws = static_cast<char*>(workspace);
+  l.chunks = reinterpret_cast<CommitChunk*>(ws);
+  l.runner = reinterpret_cast<float*>(ws + p.chunk_bytes);
+  l.merged = reinterpret_cast<CommitChunk*>(ws + p.chunk_bytes + p.runner_bytes);
+  l.rowx = nullptr;
+  l.w_bound = nullptr;
+  l.count = nullptr;
   l.B = B;
   l.S = S;
   l.K = K;
@@ -356,6 +376,87 @@ tt_status tt_lmhead_commit(int32_t B, int32_t S, int32_t K, int32_t V, const voi
   if (e != hipSuccess) return TT_ERR_HIP;
   e = launch_commit_decide(c, stream);
   if (ev[2]) (void)hipEventRecord(ev[2], stream);
+  return e == hipSuccess ? TT_OK : TT_ERR_HIP;
+}
+
+tt_status tt_lmhead_weight_bound(const void* weight, int32_t V, int32_t K, float* bound, hipStream_t stream) {
+  if (V < 0 || K < 1) return TT_ERR_INVALID_ARG;
+  if ((long long)V * K >= (1LL << 40)) return TT_ERR_UNSUPPORTED;
+  if (!bound || (V > 0 && !weight)) return TT_ERR_INVALID_ARG;
+  return launch_lmhead_weight_bound(weight, V, K, bound, stream) == hipSuccess ? TT_OK : TT_ERR_HIP;
+}
+
+size_t tt_lmhead_commit_exact_workspace(int32_t B, int32_t S, int32_t K, int32_t V) {
+  LmPlan p;
+  if (plan_lmhead(B, S, K, V, &p) != TT_OK) return 0;
+  return p.exact_total();
+}
+
+tt_status tt_lmhead_commit_exact(int32_t B, int32_t S, int32_t K, int32_t V, const void* hidden,
+                                 const void* weight, const uint8_t* mask, float gamma, const float* w_bound,
+                                 int32_t* token_id, uint8_t* committed, float* conf, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  LmPlan p;
+  tt_status st = plan_lmhead(B, S, K, V, &p);
+  if (st != TT_OK) return st;
+  if (isnan(gamma)) return TT_ERR_INVALID_ARG;
+  if (B == 0) return TT_OK;
+  if (!hidden || !weight || !mask || !w_bound || !token_id || !committed) return TT_ERR_INVALID_ARG;
+  if (((uintptr_t)hidden | (uintptr_t)weight) % 16 != 0) return TT_ERR_UNSUPPORTED;  // 16-byte loads
+  const size_t need = tt_lmhead_commit_exact_workspace(B, S, K, V);
+  if (!workspace || workspace_bytes < need) return TT_ERR_WORKSPACE;
+
+  char* ws = static_cast<char*>(workspace);
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    char* q = ws + off;
+    off += n;
+    return q;
+  };
+  LmHeadArgs l;
+  l.hidden = hidden;
+  l.weight = weight;
+  l.mask = mask;
+  l.chunks = reinterpret_cast<CommitChunk*>(take(p.chunk_bytes));
+  l.runner = reinterpret_cast<float*>(take(p.runner_bytes));
+  l.merged = reinterpret_cast<CommitChunk*>(take(p.merged_bytes));
+  l.rowx = reinterpret_cast<double*>(take(p.rowx_bytes));
+  l.w_bound = w_bound;
+  LmExactArgs x;
+  x.flags = reinterpret_cast<int*>(take(p.flags_bytes));
+  x.list = reinterpret_cast<int*>(take(p.list_bytes));
+  x.count = reinterpret_cast<int*>(take(p.count_bytes));
+  x.seq_state = reinterpret_cast<int*>(take(p.state_bytes));
+  x.need = reinterpret_cast<uint8_t*>(take(p.need_bytes));
+  x.exact = reinterpret_cast<ExactChunk*>(take(p.exact_bytes));
+  l.count = x.count;
+  l.B = B;
+  l.S = S;
+  l.K = K;
+  l.V = V;
+  l.NRG = p.NRG;
+  l.NVT = p.NVT;
+  x.hidden = hidden;
+  x.weight = weight;
+  x.mask = mask;
+  x.chunks = l.chunks;
+  x.merged = l.merged;
+  x.rowx = l.rowx;
+  x.gamma = gamma;
+  x.token_id = token_id;
+  x.committed = committed;
+  x.conf = conf;
+  x.B = B;
+  x.S = S;
+  x.K = K;
+  x.V = V;
+  x.NVT = p.NVT;
+
+  hipError_t e = launch_lmhead_reduce(l, stream);
+  if (e == hipSuccess) e = launch_lmhead_merge(l, stream);
+  if (e == hipSuccess) e = launch_lmhead_flag(x, stream);
+  if (e == hipSuccess) e = launch_lmhead_exact(x, stream);
+  if (e == hipSuccess) e = launch_lmhead_final(x, stream);
   return e == hipSuccess ? TT_OK : TT_ERR_HIP;
 }
 

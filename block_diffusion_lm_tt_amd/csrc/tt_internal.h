@@ -118,7 +118,13 @@ struct LmHeadArgs {
   const void* weight;   // [V][K] bf16
   const uint8_t* mask;  // [B*S]
   CommitChunk* chunks;  // [B*S][NVT]
+  float* runner;        // [B*S][NVT]: the chunk's runner-up logit (a second copy of the max
+                        // when it occurs twice; -inf when the chunk holds one entry)
   CommitChunk* merged;  // [B*S], one record per masked row
+  double* rowx;         // [B*S][2]: the row's runner-up logit and the bound on |fp32 logit -
+                        // exact logit| (exact mode; else unused)
+  const float* w_bound; // device: an upper bound on max_v ||weight[v]||_2, or null (estimates only)
+  int* count;           // device: flagged-row counter, zeroed by the merge (exact mode), or null
   int B, S, K, V;
   int NRG;              // row groups: ceil(B*S / 128)
   int NVT;              // vocabulary tiles: ceil(V / 256)
@@ -127,6 +133,41 @@ struct LmHeadArgs {
 // the head + reduction kernel (chunk records), and the per-row merge of those into merged[]
 hipError_t launch_lmhead_reduce(const LmHeadArgs& a, hipStream_t s);
 hipError_t launch_lmhead_merge(const LmHeadArgs& a, hipStream_t s);
+
+// ---- exact mode of the fused LM head + commit: rows whose token or decision the fp32
+// logits cannot settle are recomputed in fp64 from the hidden and head rows
+struct ExactChunk {  // per (flagged row, vocabulary tile): exact max, lowest argmax, sum of exp
+  double m;
+  int32_t tok;
+  int32_t pad;
+  double z;
+};
+
+struct LmExactArgs {
+  const void* hidden;         // [B*S][K] bf16
+  const void* weight;         // [V][K] bf16
+  const uint8_t* mask;        // [B*S]
+  const CommitChunk* chunks;  // [B*S][NVT] fp32-logit tile records
+  const CommitChunk* merged;  // [B*S] fp32-logit estimates
+  const double* rowx;         // [B*S][2] runner-up and error bound
+  int* flags;                 // [B*S]: list slot of a recomputed row, else -1
+  int* list;                  // [B*S] recomputed rows, in arrival order
+  int* count;                 // number of recomputed rows
+  int* seq_state;             // [B]: fallback state of each sequence (see lmhead_exact.hip)
+  uint8_t* need;              // [B*S (list order)][NVT]: tiles to recompute
+  ExactChunk* exact;          // [B*S (list order)][NVT]
+  float gamma;
+  int32_t* token_id;
+  uint8_t* committed;
+  float* conf;
+  int B, S, K, V, NVT;
+};
+
+hipError_t launch_lmhead_flag(const LmExactArgs& a, hipStream_t s);
+hipError_t launch_lmhead_exact(const LmExactArgs& a, hipStream_t s);
+hipError_t launch_lmhead_final(const LmExactArgs& a, hipStream_t s);
+// the weight bound of exact mode: out = an upper bound on max_v ||weight[v]||_2
+hipError_t launch_lmhead_weight_bound(const void* weight, int V, int K, float* out, hipStream_t s);
 
 // ---------------------------------------------------------------------------------------
 // the denoiser's Mamba-2 scan from the seeded state, and adaLN-single modulation

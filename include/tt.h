@@ -186,7 +186,7 @@ tt_status tt_commit_noalloc(int32_t B, int32_t S, int32_t V, int32_t dtype, cons
  *   token_id   [B, S]      int32 (device, written; -1 at unmasked positions)
  *   committed  [B, S]      uint8 (device, written)
  *   conf       [B, S]      float, may be NULL (device, written; 0 at unmasked positions)
- *   workspace  device memory of tt_lmhead_commit_workspace(B, S, K, V) bytes (16 bytes per
+ *   workspace  device memory of tt_lmhead_commit_workspace(B, S, K, V) bytes (20 bytes per
  *              position and 256-entry vocabulary chunk, plus 16 per position); contents on
  *              entry are ignored
  *
@@ -200,6 +200,52 @@ tt_status tt_lmhead_commit(int32_t B, int32_t S, int32_t K, int32_t V, const voi
                            const void *weight, const uint8_t *mask, float gamma,
                            int32_t *token_id, uint8_t *committed, float *conf, void *workspace,
                            size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * tt_lmhead_commit_exact -- tt_lmhead_commit whose integer outputs are those of exact
+ * arithmetic on the bf16 inputs.
+ *
+ * Same definition and arguments as tt_lmhead_commit, with one more input:
+ *   w_bound    float (device, read): an upper bound on max_v ||weight[v,:]||_2, as written by
+ *              tt_lmhead_weight_bound for this weight (compute it once per weight)
+ * Every fp32 logit lies within eps = 2 K 2^-24 ||hidden[b,i,:]||_2 w_bound of its exact value
+ * (bf16 products are exact in fp32; at most K roundings, each within one unit of the sum of
+ * the magnitudes). A position whose token (top two logits within 2 eps), threshold test
+ * (conf within a factor exp(2 eps + 1e-4) of gamma) or fallback (more than one position
+ * whose confidence interval reaches the largest lower bound) the fp32 values cannot settle
+ * is recomputed in fp64 on the device (all vocabulary tiles when its decision is open, the
+ * tiles whose fp32 max is within 2 eps of the row max when only its token is open) and
+ * decided on those values: token_id and committed then equal the exact-arithmetic rule's
+ * except where a margin lies below fp64 rounding. conf is the fp64 value for a position
+ * recomputed over the whole vocabulary, else the fp32-logit estimate. A recomputed row
+ * costs a pass over the head rows in fp64 (about K V fp64 multiply-adds); how many rows are
+ * recomputed depends on eps and the logits.
+ *
+ *   workspace  device memory of tt_lmhead_commit_exact_workspace(B, S, K, V) bytes
+ *              (per position and vocabulary chunk 45 bytes, plus about 40 per position)
+ *
+ * Supported: as tt_lmhead_commit. Errors as tt_lmhead_commit; w_bound NULL is
+ * TT_ERR_INVALID_ARG.
+ * ------------------------------------------------------------------------------------- */
+size_t tt_lmhead_commit_exact_workspace(int32_t B, int32_t S, int32_t K, int32_t V);
+
+tt_status tt_lmhead_commit_exact(int32_t B, int32_t S, int32_t K, int32_t V, const void *hidden,
+                                 const void *weight, const uint8_t *mask, float gamma,
+                                 const float *w_bound, int32_t *token_id, uint8_t *committed,
+                                 float *conf, void *workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * tt_lmhead_weight_bound -- the head-row norm bound of tt_lmhead_commit_exact.
+ *
+ *   weight  [V, K] bf16 (device, read)
+ *   bound   float (device, written): max_v ||weight[v,:]||_2 (fp64 sums of the exact squares),
+ *           rounded up to fp32
+ * Supported: V >= 0, K >= 1, V*K < 2^40. Errors: TT_ERR_INVALID_ARG for a negative V, K < 1
+ * or a NULL pointer (weight may be NULL when V == 0), TT_ERR_UNSUPPORTED past the size limit.
+ * ------------------------------------------------------------------------------------- */
+tt_status tt_lmhead_weight_bound(const void *weight, int32_t V, int32_t K, float *bound,
+                                 hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------
  * tt_ctx_append -- context cache update after a block is committed.

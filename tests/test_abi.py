@@ -131,7 +131,8 @@ def test_commit_validation():
 def test_lmhead_commit_validation():
     L = tt.lib()
     need = L.tt_lmhead_commit_workspace(32, 16, 4096, 131072)
-    assert need == 32 * 16 * 513 * 16  # 16-byte records: per position and 256-entry chunk, then per position
+    # per position and 256-entry chunk a 16-byte record and a 4-byte runner-up, then 16 bytes per position
+    assert need == 32 * 16 * 512 * 16 + 32 * 16 * 512 * 4 + 32 * 16 * 16
     assert L.tt_lmhead_commit_workspace(1, 1, 100, 10) == 0    # K not a multiple of 64
     assert L.tt_lmhead_commit_workspace(1, 0, 64, 10) == 0
     assert L.tt_lmhead_commit_workspace(5, 1000, 64, 10) == 0  # B*S > 4096
@@ -152,6 +153,31 @@ def test_lmhead_commit_validation():
     assert call(args(n=need - 1)) == WORKSPACE
     assert call(args(ws=None)) == WORKSPACE
     assert call(args(B=0, h=None, w=None)) == 0
+
+
+def test_lmhead_exact_validation():
+    L = tt.lib()
+    need = L.tt_lmhead_commit_exact_workspace(32, 16, 4096, 131072)
+    rows, nvt = 32 * 16, 512
+    assert need == rows * nvt * (16 + 4 + 1 + 24) + rows * (16 + 16 + 4 + 4) + 256 + 32 * 4 + 128
+    assert L.tt_lmhead_commit_exact_workspace(1, 1, 100, 10) == 0
+    args = lambda **kw: dict(dict(B=32, S=16, K=4096, V=131072, h=FAKE, w=FAKE, mk=FAKE, g=0.8, wb=FAKE,  # noqa
+                                  tok=FAKE, com=FAKE, conf=None, ws=FAKE, n=need), **kw)
+    call = lambda a: L.tt_lmhead_commit_exact(a["B"], a["S"], a["K"], a["V"], a["h"], a["w"], a["mk"],  # noqa
+                                              a["g"], a["wb"], a["tok"], a["com"], a["conf"], a["ws"], a["n"],
+                                              None)
+    assert call(args(g=float("nan"))) == INVALID
+    for k in ("h", "w", "mk", "wb", "tok", "com"):
+        assert call(args(**{k: None})) == INVALID
+    assert call(args(K=100)) == UNSUPPORTED
+    assert call(args(h=FAKE + 2)) == UNSUPPORTED
+    assert call(args(n=need - 1)) == WORKSPACE
+    assert call(args(B=0, h=None, w=None, wb=None)) == 0
+    assert L.tt_lmhead_weight_bound(FAKE, -1, 64, FAKE, None) == INVALID
+    assert L.tt_lmhead_weight_bound(FAKE, 10, 0, FAKE, None) == INVALID
+    assert L.tt_lmhead_weight_bound(FAKE, 10, 64, None, None) == INVALID
+    assert L.tt_lmhead_weight_bound(None, 10, 64, FAKE, None) == INVALID
+    assert L.tt_lmhead_weight_bound(FAKE, 1 << 30, 1 << 20, FAKE, None) == UNSUPPORTED
 
 
 @pytest.mark.parametrize("kw,want", [

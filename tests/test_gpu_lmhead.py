@@ -242,3 +242,103 @@ def test_misaligned_operands_are_refused(dev):
     h2.copy_(h)
     with pytest.raises(tt.TTError, match="UNSUPPORTED"):
         tt.tt_lmhead_commit(h2, w, m, 0.5)
+
+
+# ---- exact mode (tt_lmhead_commit_exact): integer outputs equal the oracle's --------------
+
+def _gpu_exact(x: W.LmHeadInputs, dev, gamma=None):
+    import block_diffusion_lm_tt_amd as tt
+    h, w, m = TZ.lmhead_to_device(x, dev)
+    wb = tt.tt_lmhead_weight_bound(w)
+    tok, com, conf = tt.tt_lmhead_commit(h, w, m, x.gamma if gamma is None else gamma, w_bound=wb)
+    torch.cuda.synchronize()
+    return tok.cpu().numpy(), com.cpu().numpy(), conf.double().cpu().numpy()
+
+
+def _check_exact(x: W.LmHeadInputs, got, gamma, what):
+    want = _exact(x, gamma)
+    tok_o, com_o = want[0], want[1]
+    assert np.array_equal(got[0], tok_o), (what, "tokens", np.argwhere(got[0] != tok_o)[:5])
+    assert np.array_equal(got[1], com_o), (what, "decisions", np.argwhere(got[1] != com_o)[:5])
+    _check(x, got, want, gamma, what)  # confidences within the fp32 bound (exact where recomputed)
+
+
+def test_lmhead_weight_bound(dev):
+    import block_diffusion_lm_tt_amd as tt
+    rng = np.random.default_rng(3)
+    w = rng.normal(0.0, 0.05, size=(3001, 320)).astype(np.float32)
+    w[1777] *= 7.0  # the largest row
+    wb = W.f32_to_bf16_bits(w)
+    got = float(tt.tt_lmhead_weight_bound(TZ.to_torch(wb, W.BF16, dev)).cpu()[0])
+    norms = np.sqrt((W.bf16_bits_to_f32(wb).astype(np.float64) ** 2).sum(1))
+    _say(f"[lmhead] weight bound {got:.9g} vs max row norm {norms.max():.9g}")
+    assert norms.max() <= got <= norms.max() * (1 + 1e-6)
+
+
+EXACT_RAND = [
+    ("k192-v1000", 2, 8, 192, 1000, 0.6),
+    ("k4096-v4096", 4, 16, 4096, 4096, 0.8),
+    ("k1024-v33000-ragged", 3, 16, 1024, 33000, 0.8),
+    ("k256-v2000-all-masked", 4, 16, 256, 2000, 0.05),
+]
+
+
+@pytest.mark.parametrize("case", EXACT_RAND, ids=[c[0] for c in EXACT_RAND])
+def test_lmhead_exact_random(dev, case):
+    name, B, S, K, V, gamma = case
+    _say(f"[lmhead exact] {name}")
+    mask = np.ones((B, S), np.uint8) if "all" in name else W.random_mask(B, S, 2, S, seed=3)
+    x = W.make_lmhead(B, S, K, V, seed=V + K + 1, gamma=gamma, mask=mask, peaks=C3_PEAKS)
+    _check_exact(x, _gpu_exact(x, dev), gamma, name)
+
+
+@pytest.mark.parametrize("gamma", [0.0, 1.5, float("inf"), -1.0])
+def test_lmhead_exact_gamma_edges(dev, gamma):
+    x = W.make_lmhead(3, 16, 256, 2000, seed=21, gamma=gamma, mask=W.random_mask(3, 16, 0, 16, seed=8),
+                      peaks=C3_PEAKS)
+    _check_exact(x, _gpu_exact(x, dev), gamma, f"exact gamma={gamma}")
+
+
+def test_lmhead_exact_integer_data(dev):
+    x = _int_case(20, 16, 128, 1000, seed=147, mask=W.random_mask(20, 16, 4, 16, seed=128))
+    _check_exact(x, _gpu_exact(x, dev), x.gamma, "exact integer")
+
+
+def test_lmhead_exact_near_ties(dev):
+    # margins far below the fp32 error bound, where the estimates cannot decide:
+    #  - sequence 0: two positions whose hidden rows differ in one feature by one bf16 step
+    #    (fallback between nearly equal confidences) and two identical rows (an exact tie:
+    #    the lower position wins);
+    #  - sequence 1: a row aimed at two head rows that differ in one feature by one bf16 step
+    #    (top-2 logits nearly tied);
+    #  - sequence 2: gamma set to a position's exact confidence rounded to fp32 (threshold).
+    _say("[lmhead exact] near ties")
+    B, S, K, V = 3, 16, 512, 3000
+    x = W.make_lmhead(B, S, K, V, seed=77, gamma=0.3, mask=np.ones((B, S), np.uint8), peaks=C3_PEAKS)
+    hid, wgt = x.hidden.copy(), x.weight.copy()
+    hid[0, 5] = hid[0, 2]
+    hid[0, 5, 17] = hid[0, 5, 17] + 1  # one bf16 step
+    hid[0, 9] = hid[0, 3]
+    wgt[1201] = wgt[1200]
+    wgt[1201, 40] = wgt[1201, 40] + 1
+    wf = W.bf16_bits_to_f32(wgt[1200]).astype(np.float64)
+    hid[1, 4] = W.f32_to_bf16_bits((12.0 * wf / np.dot(wf, wf)).astype(np.float32))
+    y = W.LmHeadInputs(B, S, K, V, hid, wgt, x.mask, x.gamma)
+    _, _, conf_o, _ = _exact(y, 0.3)
+    # for sequence 2 the gamma of the whole call cannot differ per sequence: take the row's
+    # confidence as gamma for a second call on sequence 2 alone
+    _check_exact(y, _gpu_exact(y, dev), 0.3, "near ties")
+    z = _sub(y, [2])
+    g2 = float(np.float32(conf_o[2, 7]))
+    _check_exact(z, _gpu_exact(z, dev, gamma=g2), g2, "gamma at a confidence")
+
+
+def test_lmhead_exact_full_size_sampled(dev):
+    _say("[lmhead exact] full size B32 S16 K4096 V131072")
+    w3 = W.WORKLOADS[3]
+    x = W.make_lmhead(w3.B, w3.S, 4096, w3.V, seed=w3.seed, gamma=w3.gamma,
+                      mask=W.random_mask(w3.B, w3.S, 4, 16, seed=w3.seed), peaks=C3_PEAKS)
+    tok, com, conf = _gpu_exact(x, dev)
+    seqs = [0, w3.B - 1]
+    y = _sub(x, seqs)
+    _check_exact(y, (tok[seqs], com[seqs], conf[seqs]), x.gamma, "exact full size")
