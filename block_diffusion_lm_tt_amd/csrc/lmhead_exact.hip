@@ -20,7 +20,7 @@
 //     for a row whose token alone is open (the exact argmax cannot lie elsewhere). Settled
 //     outputs are written here.
 //  2. lmhead_exact (one workgroup per vocabulary tile, each lane one head row): the listed
-//     rows that need the tile, four at a time: fp64 dot products (each bf16 product exact,
+//     rows that need the tile, eight at a time: fp64 dot products (each bf16 product exact,
 //     fp64 sums), then per row the tile's exact max, lowest argmax and sum of exp in fp64.
 //     A tile no listed row needs costs one load of the counter and of its flags.
 //  3. lmhead_final (one workgroup per sequence with a listed row): merges each listed row's
@@ -37,7 +37,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int FT = 256;              // threads of the per-sequence kernels
 constexpr int kMaxS = 1024;
 constexpr double kZBand = 1e-4;      // the fp32 evaluation of Z, relative (about 1e-5)
-constexpr int EXB = 4;               // listed rows per pass of the exact kernel
+constexpr int EXB = 8;               // listed rows per pass of the exact kernel
 constexpr int KB = 512;              // features per LDS block of the exact kernel
 
 __device__ __forceinline__ double bf(uint16_t x) { return (double)__uint_as_float(((uint32_t)x) << 16); }
@@ -132,20 +132,29 @@ __global__ __launch_bounds__(FT) void lmhead_flag_kernel(LmExactArgs a) {
   }
   if (tid == 0) a.seq_state[b] = state;
   __syncthreads();
-  // list the rows left open and mark the tiles each needs
+  // list the rows left open, then mark the tiles each needs (the whole workgroup per row)
+  __shared__ int s_slot[kMaxS];
   for (int i = tid; i < a.S; i += FT) {
+    s_slot[i] = -1;
     if (s_dec[i] == 255 || (s_dec[i] != 2 && !s_tok[i])) continue;
     const size_t r = (size_t)b * a.S + i;
     const int slot = atomicAdd(a.count, 1);
     a.flags[r] = slot;
     a.list[slot] = (int)r;
+    s_slot[i] = slot;
+  }
+  __syncthreads();
+  for (int i = 0; i < a.S; ++i) {
+    const int slot = s_slot[i];
+    if (slot < 0) continue;
+    const size_t r = (size_t)b * a.S + i;
     uint8_t* need = a.need + (size_t)slot * a.NVT;
     if (s_dec[i] == 2) {
-      for (int t = 0; t < a.NVT; ++t) need[t] = 1;
+      for (int t = tid; t < a.NVT; t += FT) need[t] = 1;
     } else {
       const CommitChunk* ch = a.chunks + r * a.NVT;
       const double lim = (double)a.merged[r].m - 2.0 * a.rowx[2 * r + 1];
-      for (int t = 0; t < a.NVT; ++t) need[t] = (double)ch[t].m >= lim;
+      for (int t = tid; t < a.NVT; t += FT) need[t] = (double)ch[t].m >= lim;
     }
   }
 }
@@ -333,10 +342,22 @@ __global__ __launch_bounds__(256) void weight_bound_kernel(const uint16_t* W, in
   double best = 0.0;
   for (int v = blockIdx.x * 4 + w; v < V; v += gridDim.x * 4) {
     const uint16_t* row = W + (size_t)v * K;
-    double s = 0.0;
-    for (int k = lane; k < K; k += 64) {
-      const double x = bf(row[k]);
-      s = fma(x, x, s);  // exact squares; fp64 sums
+    double s = 0.0;  // exact squares, fp64 sums
+    if (K % 8 == 0 && (reinterpret_cast<uintptr_t>(W) & 15) == 0) {
+      for (int k = lane * 8; k < K; k += 512) {
+        const u32x4 q = *reinterpret_cast<const u32x4*>(row + k);
+        const uint16_t* e = reinterpret_cast<const uint16_t*>(&q);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const double x = bf(e[u]);
+          s = fma(x, x, s);
+        }
+      }
+    } else {
+      for (int k = lane; k < K; k += 64) {
+        const double x = bf(row[k]);
+        s = fma(x, x, s);
+      }
     }
     for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
     best = fmax(best, s);
