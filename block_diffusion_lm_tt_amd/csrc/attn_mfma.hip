@@ -22,9 +22,9 @@
 //    about the same for every cluster.
 //    A cluster range that covers a whole unit writes the final output; a unit cut by a
 //    range boundary leaves per-piece partials (running max and sum in fp32, normalised O
-//    in bf16) that the combine kernel merges with a log-sum-exp rescale. The cluster that
-//    holds a cut unit's last piece leaves a record of the unit for the combine kernel,
-//    which then touches nothing else.
+//    in bf16) that the combine kernel merges with a log-sum-exp rescale. The cluster whose
+//    segment ends a unit leaves the unit's merge record (none when it held the unit whole);
+//    the combine's grid is one row of workgroups per unit, and it touches nothing else.
 //  * K and V tiles go HBM -> LDS directly (global_load_lds_dwordx4, no staging registers)
 //    into a ring of 8 stages of 16 KB (8 KB of keys + 8 KB of values): six tiles are in
 //    flight per CU while two are in use; explicit vmcnt waits and one barrier per tile.
@@ -476,9 +476,6 @@ __global__ __launch_bounds__(NTHR, 1) void attn_mfma_kernel(AttnArgs a) {
   int pb = __builtin_amdgcn_readfirstlane(P[bcur]);
   bcur = __builtin_amdgcn_readfirstlane(bcur);
   __syncthreads();  // P lives in the ring; done with it
-  // merge record of this cluster: none, unless its first segment is the last piece of a
-  // cut unit (written again there, by the same thread)
-  if (qs == 0 && tid == 0) *reinterpret_cast<int4*>(a.rec + 4 * cluster) = int4{-1, 0, 0, T};
   if (t0 >= t1) {
     // an empty range (only when T < NC): its slot-0 piece is marked empty (l = 0) for the
     // combine, which may meet it between the first and the last piece of a cut unit
@@ -541,12 +538,19 @@ __global__ __launch_bounds__(NTHR, 1) void attn_mfma_kernel(AttnArgs a) {
     if (te <= ta) continue;  // the range ends among the unit's overhead positions
     const bool whole = (ta == 0 && te == nt);
     const int slot = first_seg ? 0 : 1;
-    if (first_seg && ta > 0 && te == nt && qs == 0 && wave == 0 && fresh_lane() == 0) {  // last piece of a cut unit
-      const int cf = cluster_of(ustart + SC, T, a.NC);
-      const int cs = 2 * cf + (range_start(cf, T, a.NC) < ustart ? 1 : 0);
-      int cl = __builtin_amdgcn_readfirstlane(cluster);
-      asm volatile("" : "+s"(cl));  // the address is formed here, not kept across the loop
-      *reinterpret_cast<int4*>(a.rec + 4 * cl) = int4{bcur, g, cs, T};
+    if (te == nt && qs == 0 && wave == 0 && fresh_lane() == 0) {
+      // the unit's merge record, by the cluster whose segment ends the unit: none for a whole
+      // unit; for a cut one (its last piece is always the cluster's first segment) the first
+      // piece's cluster and slot and this cluster, the last piece's
+      int4 r = int4{-1, 0, 0, 0};
+      if (ta > 0) {
+        const int cf = cluster_of(ustart + SC, T, a.NC);
+        const int cs = 2 * cf + (range_start(cf, T, a.NC) < ustart ? 1 : 0);
+        r = int4{bcur, g, cs, cluster};
+      }
+      int u = __builtin_amdgcn_readfirstlane(bcur * a.Hkv + g);
+      asm volatile("" : "+s"(u));  // the address is formed here, not kept across the loop
+      *reinterpret_cast<int4*>(a.rec + 4 * u) = r;
     }
     first_seg = false;
     const int n = te - ta;  // tiles in this segment (>= 1)
@@ -701,14 +705,13 @@ __global__ __launch_bounds__(NTHR, 1) void attn_mfma_kernel(AttnArgs a) {
 // read eight at a time, all loads in flight together, and merged with a running max.
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   constexpr int PB = 8;
-  // grid: (row chunk, cluster): the row chunks of one record are consecutive workgroups, so
-  // they spread over the XCDs (workgroup id % 8) whatever the cluster of the record
-  const int c_last = bid_y();
+  // grid: (row chunk, unit): the row chunks of one record are consecutive workgroups, so
+  // they spread over the XCDs (workgroup id % 8)
   // the record was written by the previous kernel: scalar loads, uniform arithmetic
-  const c_i32* rec = (c_i32*)(uintptr_t)(a.rec + 4 * c_last);
+  const c_i32* rec = (c_i32*)(uintptr_t)(a.rec + 4 * bid_y());
   const int b = rec[0];
   if (b < 0) return;
-  const int g = rec[1], c_first = rec[2] >> 1, first_slot = rec[2] & 1;
+  const int g = rec[1], c_first = rec[2] >> 1, first_slot = rec[2] & 1, c_last = rec[3];
   const int rows_unit = a.G * a.S;
   const int r = bid_x() * 16 + (tid_x() >> 4);
   if (r >= rows_unit) return;
@@ -769,7 +772,7 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s, hipEvent_t ev0, hi
   if (e != hipSuccess) return e;
   if (ev1) (void)hipEventRecord(ev1, s);
   const int rows_unit = a.G * a.S;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3((rows_unit + 15) / 16, a.NC), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((rows_unit + 15) / 16, a.B * a.Hkv), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

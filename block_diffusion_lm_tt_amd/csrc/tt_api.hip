@@ -45,7 +45,7 @@ tt_status plan_attn(const tt_attn_shape* sh, AttnPlan* p) {
   nc = nc / 8 * 8;
   p->NC = nc < 8 ? 8 : nc;
   if (p->mfma) {
-    p->plan_bytes = align_up((size_t)p->NC * 4 * sizeof(int32_t));
+    p->plan_bytes = align_up((size_t)sh->B * sh->Hkv * 4 * sizeof(int32_t));
     p->part_bytes = align_up(attn_part_bytes(p->NC, p->NQ));
   } else {
     p->plan_bytes = p->part_bytes = 0;

@@ -36,9 +36,9 @@ struct AttnArgs {
   const int32_t* ctx_len;
   void* o;
   float* part;        // partial results per (cluster, segment, query slice)
-  int32_t* rec;       // [NC][4] merge records: per cluster, the cut unit whose last piece it
-                      // holds (b, g, 2 * first cluster + first piece's slot, list length)
-                      // or b = -1; written by the main kernel, read by the combine
+  int32_t* rec;       // [B*Hkv][4] merge records: per unit (b, g), b = -1 for a unit one
+                      // cluster holds whole, else (b, g, 2 * first piece's cluster + its slot,
+                      // last piece's cluster); written by the main kernel, read by the combine
   int B, S, Hq, Hkv, G, D, Lmax;
   int NQ;             // workgroups (query slices) per (sequence, KV head) unit
   int NC;             // clusters; each owns a contiguous range of the global position list
