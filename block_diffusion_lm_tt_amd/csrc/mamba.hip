@@ -160,8 +160,10 @@ __device__ __forceinline__ void chunk_store(const ChunkRegs<NW, NM>& r, MmaSmem<
   }
 }
 
+// (at least four waves per SIMD: within 128 registers, four workgroups of four waves per CU
+// keep their state loads in flight; the compiler fits the headline shape without spills)
 template <int NW, int NM>
-__global__ __launch_bounds__(64 * NW) void mamba2_scan_mfma_kernel(MambaArgs a) {
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 8))) void mamba2_scan_mfma_kernel(MambaArgs a) {
   constexpr int N = 32 * NM, P = 16 * NW, NT2 = 2 * NM;
   using Sm = MmaSmem<NW, NM>;
   __shared__ Sm sm;
