@@ -208,6 +208,8 @@ def loop_bench(w, args, torch, tt, TZ, W):
                       "ctx_len": int(w.ctx_lens()[0]), "layers": L, "steps": T, "V": w.V,
                       "reps": reps},
            "attn_mfma_TFLOPs_gamma_0.8": attn_flop / (results[1]["ms_per_block"] * 1e-3) / 1e12,
+           "attn_mfma_pct_bf16_peak_gamma_0.8":
+               100.0 * attn_flop / (results[1]["ms_per_block"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
            "ctx_append_us_per_layer": append_us,
            "ctx_append_GBps": append_bytes / append_us / 1e3,
            "sweep": results}

@@ -309,8 +309,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 8)))
 // NPT: state columns per thread (N / (256 / P)), a compile-time bound on the registers
 template <typename T, int NPT>
 __global__ __launch_bounds__(NT) void mamba2_scan_kernel(MambaArgs a) {
-  __shared__ float sC[CH][kMambaMaxN];
-  __shared__ float sB[CH][kMambaMaxN];
+  // rows padded by one word: the chunk matrix reads 16 rows of B (and 4 of C) at one column
+  __shared__ float sC[CH][kMambaMaxN + 1];
+  __shared__ float sB[CH][kMambaMaxN + 1];
   __shared__ float sX[CH][kMambaMaxP];
   __shared__ float sM[CH][CH];
   __shared__ float sL[CH], sDelta[CH];

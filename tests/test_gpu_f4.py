@@ -188,3 +188,43 @@ def test_adaln_gate_matches_oracle(dev, dtype, d):
     ex = np.abs(got - want) / bound
     _say(f"gate {dtype} d={d}: max-abs err {np.abs(got - want).max():.3e}, worst fraction {ex.max():.3f}")
     assert ex.max() <= 1.0
+
+
+def test_scan_longest_block(dev):
+    # S = 1024 positions (64 chunks, the longest block the entry point takes), bf16
+    m = W.make_mamba(1, 1024, 2, 64, 128, 1, W.BF16, seed=1024)
+    _check_scan(m, dev, "S=1024")
+
+
+def test_scan_unaligned_inputs_take_the_vector_path(dev):
+    # x, B and C off a 16-byte boundary run the vector-ALU kernel; same bars
+    import block_diffusion_lm_tt_amd as tt
+    from oracle import ttref_mamba2_scan
+    m = W.make_mamba(2, 20, 4, 64, 128, 2, W.BF16, seed=43)
+    x, dt, bias, Al, Dk, Bm, Cm, h0 = TZ.mamba_to_device(m, dev)
+
+    def off(t):
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=dev)
+        v = buf[1:].view(t.shape)
+        v.copy_(t)
+        return v
+    y, h = tt.tt_mamba2_seeded_scan(off(x), dt, bias, Al, Dk, off(Bm), off(Cm), h0, G=2, want_state=True)
+    torch.cuda.synchronize()
+    yr, hr = ttref_mamba2_scan(m.B, m.S, m.H, m.P, m.N, m.G, m.dtype, m.x, m.dt, m.dt_bias, m.A_log, m.Dskip,
+                               m.Bm, m.Cm, m.h0)
+    T, Hb = _scan_bound(m)
+    assert (np.abs(y.double().cpu().numpy() - yr) <= 2.0 ** -8 * np.abs(yr) + 2.0 ** -15 * T).all()
+    assert (np.abs(h.double().cpu().numpy() - hr) <= 2.0 ** -15 * Hb).all()
+
+
+def test_scan_and_adaln_empty_batch(dev):
+    import block_diffusion_lm_tt_amd as tt
+    m = W.make_mamba(1, 4, 2, 64, 128, 1, W.BF16, seed=1)
+    args = [t[:0] if t.dim() > 1 else t for t in TZ.mamba_to_device(m, dev)]
+    y, h = tt.tt_mamba2_seeded_scan(*args, G=1, want_state=True)
+    assert y.numel() == 0 and h.numel() == 0
+    a = W.make_adaln(1, 2, 64, W.BF16, seed=1)
+    x, f, tm, tab = TZ.adaln_to_device(a, dev)
+    assert tt.tt_adaln_modulate(x[:0], tm[:0], tab).numel() == 0
+    assert tt.tt_adaln_gate(x[:0], f[:0], tm[:0], tab).numel() == 0
+    torch.cuda.synchronize()
