@@ -255,6 +255,32 @@ def stream_read_ceiling(torch, dev) -> dict:
     return out
 
 
+def mfma_rate(torch, dev) -> float:
+    """The matrix cores' bf16 rate measured in the same run: the probe kernel of libttprobe.so
+    (v_mfma_f32_32x32x16_bf16 back to back in four independent chains per wave, two waves per
+    SIMD on every CU), best of three, in TFLOP/s."""
+    import ctypes
+    from block_diffusion_lm_tt_amd.build import PROBE_LIB
+    L = ctypes.CDLL(PROBE_LIB)
+    L.ttprobe_mfma_rate.restype = ctypes.c_int
+    L.ttprobe_mfma_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    blocks, iters = 512, 20000
+    sink = torch.empty((blocks,), dtype=torch.float32, device=dev)
+    st = torch.cuda.current_stream(dev)
+    flop = blocks * 4 * 4 * iters * 32768.0
+    best = 0.0
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        if L.ttprobe_mfma_rate(blocks, iters, sink.data_ptr(), st.cuda_stream) != 0:
+            raise RuntimeError("mfma-rate probe failed")
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, flop / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    log(f"[bench] bf16 matrix-core rate: {best:.0f} TFLOP/s")
+    return best
+
+
 def stream_read_same_size(torch, dev, nbytes: int) -> dict:
     """The register-streaming probe over exactly `nbytes` (four rotated buffers, so that the
     last-level cache cannot serve them), best over grid sizes of the median of five
@@ -665,6 +691,7 @@ def main():
     stream_gbs = stream["GBps"]
     same = stream_read_same_size(torch, dev, x.ctx_kv_bytes)
     same_c = stream_read_same_size(torch, dev, c.masked_row_bytes)
+    mfma_meas = mfma_rate(torch, dev)
 
     copy_probe(args, torch, dev)
 
@@ -719,6 +746,8 @@ def main():
         "commit_GBps": commit_bytes / t_commit / 1e9,
         "mfma_TFLOPs": tflops,
         "mfma_pct_bf16_peak": 100.0 * tflops / MFMA_BF16_PEAK_TFLOPS,
+        "mfma_bf16_TFLOPs_measured": mfma_meas,
+        "mfma_pct_of_measured_rate": 100.0 * tflops / mfma_meas,
         "roofline": {"kernel": "attn_mfma_kernel", "bound": "hbm", "achieved": gbs_main,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs_main / HBM_PEAK_GBS,
                      "traffic": profiled_traffic("attn_mfma_kernel")

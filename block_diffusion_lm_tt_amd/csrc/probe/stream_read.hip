@@ -5,6 +5,7 @@
 //    no load can be dropped;
 //  - LDS-DMA: every wave copies 16-byte pieces straight into LDS (global_load_lds_dwordx4,
 //    the attention kernel's way of streaming its context), eight per thread in flight.
+// And the matrix cores' bf16 rate (v_mfma_f32_32x32x16_bf16 back to back, at the end).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -86,5 +87,44 @@ extern "C" int ttprobe_stream_read(const void* src, size_t bytes, uint32_t* sink
   if (!src || !sink || blocks < 1 || bytes % 16 != 0 || (uintptr_t)src % 16 != 0) return -1;
   hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(NTH), 0, stream, static_cast<const u32x4*>(src),
                      bytes / 16, sink);
+  return (int)hipGetLastError();
+}
+
+// ---- matrix-core rate: v_mfma_f32_32x32x16_bf16 back to back -----------------------------
+// Each wave runs four independent accumulation chains (so a product never waits for the
+// previous one's result), `iters` rounds of four products, and writes one value so that no
+// product can be dropped.
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__global__ __launch_bounds__(256) void mfma_rate_kernel(int iters, float* sink) {
+  bf16x8 a, b;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    a[k] = (__bf16)(0.001f * (threadIdx.x + k));
+    b[k] = (__bf16)(0.002f * (threadIdx.x - k));
+  }
+  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int i = 0; i < iters; ++i) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) s += c0[k] + c1[k] + c2[k] + c3[k];
+  if (s == 12345.0f) sink[blockIdx.x] = s;  // practically never: keeps the products live
+}
+
+}  // namespace
+
+// blocks workgroups of four waves (one per SIMD of a CU when blocks = 256 per CU count),
+// each wave 4 * iters products of 32 x 32 x 16 (32768 flop each). Returns 0 or a HIP error.
+extern "C" int ttprobe_mfma_rate(int blocks, int iters, float* sink, hipStream_t stream) {
+  if (blocks < 1 || iters < 1 || !sink) return -1;
+  hipLaunchKernelGGL(mfma_rate_kernel, dim3(blocks), dim3(256), 0, stream, iters, sink);
   return (int)hipGetLastError();
 }
