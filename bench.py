@@ -281,6 +281,51 @@ def mfma_rate(torch, dev) -> float:
     return best
 
 
+def tile_loop_probe(torch, dev) -> dict:
+    """The attention tile loop's resources measured on every CU (probes of libttprobe.so, one
+    8-wave workgroup per CU): the LDS read rate of the K operand reads (ds_read_b128) and of
+    the V^T operand reads (ds_read_b64_tr_b16), in bytes per shader-clock cycle per CU; and the
+    cycles per iteration of the matrix/vector core (16 matrix products and one vector phase per
+    wave): matrix only, vector only, both in different waves at once, the two-barrier
+    ping-pong, the ping-pong with the next tile's operand reads (128 KB per CU), and one wave
+    per SIMD carrying both waves' work (64 rows, the same products and vector work per SIMD),
+    without and with its next tile's operand reads (64 KB per CU)."""
+    import ctypes
+    from block_diffusion_lm_tt_amd.build import PROBE_LIB
+    L = ctypes.CDLL(PROBE_LIB)
+    for f in (L.ttprobe_lds_read, L.ttprobe_tile_core):
+        f.restype = ctypes.c_int
+        f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    blocks, iters = 256, 2000
+    sink = torch.zeros((blocks * 8 + 1,), dtype=torch.float32, device=dev)
+    st = torch.cuda.current_stream(dev)
+
+    def run(fn, arg, waves):
+        for _ in range(2):  # the second launch is the one read
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            if fn(arg, blocks, iters, sink.data_ptr(), st.cuda_stream) != 0:
+                raise RuntimeError("tile-loop probe failed")
+            e1.record()
+            torch.cuda.synchronize()
+        cyc = sink[:blocks * 8].view(blocks, 8)[:, waves].mean().item() / iters
+        return cyc, e0.elapsed_time(e1) * 1e3 / iters
+
+    out = {}
+    for kind, name in ((0, "k_b128"), (1, "v_tr_b64")):
+        cyc, us = run(L.ttprobe_lds_read, kind, slice(0, 8))
+        out[f"lds_read_{name}_bytes_per_cycle_per_cu"] = 65536 / cyc
+    names = ("matrix_only", "vector_only", "both_at_once", "ping_pong", "ping_pong_with_operand_reads",
+             "one_wave_per_simd_64_rows", "one_wave_per_simd_64_rows_with_operand_reads")
+    waves = (slice(0, 4), slice(4, 8), slice(0, 8), slice(0, 8), slice(0, 8), slice(0, 4), slice(0, 4))
+    for mode, name in enumerate(names):
+        cyc, us = run(L.ttprobe_tile_core, mode, waves[mode])
+        out[f"core_{name}_cycles_per_iteration"] = cyc
+        out[f"core_{name}_us_per_iteration"] = us
+    log("[bench] tile-loop probe: " + ", ".join(f"{k} {v:.1f}" for k, v in out.items()))
+    return out
+
+
 def stream_read_same_size(torch, dev, nbytes: int) -> dict:
     """The register-streaming probe over exactly `nbytes` (four rotated buffers, so that the
     last-level cache cannot serve them), best over grid sizes of the median of five
@@ -687,11 +732,20 @@ def main():
     torch.cuda.synchronize()
     per_call = np.array([evs[k].elapsed_time(evs[k + 1]) * 1e3 for k in range(n_dist)])
     p10, p50, p90 = (float(np.percentile(per_call, p)) for p in (10, 50, 90))
+    # the commit call alone, the same way (back-to-back over the rotated logits)
+    torch.cuda.synchronize()
+    ea.record()
+    for k in range(K_PLAIN):
+        tt.tt_commit(lgs[k % R], mk, c.gamma, token_id=tok, committed=com, conf=conf, workspace=ws_c)
+    eb.record()
+    torch.cuda.synchronize()
+    t_commit_plain = ea.elapsed_time(eb) * 1e-3 / K_PLAIN
     stream = stream_read_ceiling(torch, dev)
     stream_gbs = stream["GBps"]
     same = stream_read_same_size(torch, dev, x.ctx_kv_bytes)
     same_c = stream_read_same_size(torch, dev, c.masked_row_bytes)
     mfma_meas = mfma_rate(torch, dev)
+    core = tile_loop_probe(torch, dev)
 
     copy_probe(args, torch, dev)
 
@@ -708,7 +762,8 @@ def main():
     commit_bytes = c.masked_row_bytes
     log(f"[bench] attn {t_attn_plain*1e6:.1f} us/call back-to-back ({t_attn*1e6:.1f} us with timing "
         f"events; main kernel {t_main*1e6:.1f} us), "
-        f"commit {t_commit*1e6:.1f} us/call (reduce {t_reduce*1e6:.1f} us), step {wall/K*1e3:.3f} ms")
+        f"commit {t_commit_plain*1e6:.1f} us/call back-to-back ({t_commit*1e6:.1f} us with timing events; "
+        f"reduce {t_reduce*1e6:.1f} us), step {wall/K*1e3:.3f} ms")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -742,12 +797,15 @@ def main():
         "attn_us_per_call": t_attn_plain * 1e6,
         "attn_us_per_call_p10_p50_p90": [p10, p50, p90],
         "attn_us_per_call_with_timing_events": t_attn * 1e6,
-        "commit_us_per_call": t_commit * 1e6,
-        "commit_GBps": commit_bytes / t_commit / 1e9,
+        "commit_us_per_call": t_commit_plain * 1e6,
+        "commit_GBps": commit_bytes / t_commit_plain / 1e9,
+        "commit_us_per_call_with_timing_events": t_commit * 1e6,
+        "commit_reduce_us_with_timing_events": t_reduce * 1e6,
         "mfma_TFLOPs": tflops,
         "mfma_pct_bf16_peak": 100.0 * tflops / MFMA_BF16_PEAK_TFLOPS,
         "mfma_bf16_TFLOPs_measured": mfma_meas,
         "mfma_pct_of_measured_rate": 100.0 * tflops / mfma_meas,
+        "tile_loop_probe": core,
         "roofline": {"kernel": "attn_mfma_kernel", "bound": "hbm", "achieved": gbs_main,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs_main / HBM_PEAK_GBS,
                      "traffic": profiled_traffic("attn_mfma_kernel")

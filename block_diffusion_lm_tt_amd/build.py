@@ -11,9 +11,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtt.so")
-# a measurement probe (a plain streaming read, the benchmark's bandwidth ceiling), a library of
-# its own so that it is not part of libtt's interface
-PROBE_SRC = os.path.join(CSRC, "probe", "stream_read.hip")
+# measurement probes (a plain streaming read, the benchmark's bandwidth ceiling; the matrix-core
+# rate; the attention tile loop's LDS and matrix/vector core), a library of their own so that
+# they are not part of libtt's interface
+PROBE_SRCS = [os.path.join(CSRC, "probe", "stream_read.hip"), os.path.join(CSRC, "probe", "tile_core.hip")]
 PROBE_LIB = os.path.join(HERE, "libttprobe.so")
 BUILD = os.path.join(ROOT, "_build", "libtt")
 ARCH = os.environ.get("TT_OFFLOAD_ARCH", "gfx950")
@@ -77,12 +78,12 @@ def build(verbose: bool = False) -> str:
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
     tmp = PROBE_LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-shared", PROBE_SRC, "-o", tmp]
+    cmd = [HIPCC, *FLAGS, "-shared", *PROBE_SRCS, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed for {PROBE_SRC}:\n{r.stderr}")
+        raise RuntimeError(f"hipcc failed for {PROBE_SRCS}:\n{r.stderr}")
     os.replace(tmp, PROBE_LIB)
     return LIB
 

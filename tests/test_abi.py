@@ -19,6 +19,22 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, n), f"libtt.so does not export {n}"
 
 
+def test_probe_library_exports_its_probes():
+    # the measurement probes the benchmark times its ceilings with (a library of their own)
+    from block_diffusion_lm_tt_amd.build import PROBE_LIB
+    P = ctypes.CDLL(PROBE_LIB)
+    for n in ("ttprobe_stream_read", "ttprobe_stream_read_lds", "ttprobe_mfma_rate", "ttprobe_lds_read",
+              "ttprobe_tile_core"):
+        assert hasattr(P, n), f"libttprobe.so does not export {n}"
+    # argument checks on the host, before any launch
+    P.ttprobe_tile_core.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    P.ttprobe_lds_read.argtypes = P.ttprobe_tile_core.argtypes
+    assert P.ttprobe_tile_core(7, 1, 1, ctypes.c_void_p(16), None) == -1
+    assert P.ttprobe_tile_core(0, 0, 1, ctypes.c_void_p(16), None) == -1
+    assert P.ttprobe_lds_read(2, 1, 1, ctypes.c_void_p(16), None) == -1
+    assert P.ttprobe_lds_read(0, 1, 1, None, None) == -1
+
+
 def test_build_id_matches_the_sources_beside_it():
     from block_diffusion_lm_tt_amd.build import source_hash
     L = tt.lib()
