@@ -45,6 +45,10 @@
 //    matrix, so each SIMD's two waves keep its matrix core and its VALU busy at the same
 //    time. With 32 rows per wave everything fits in 256 VGPRs (no accumulation registers,
 //    no moves between register files).
+//  * A unit of fewer than 256 query rows (small G*S) leaves waves whose 32 rows all lie past
+//    it: those waves copy their share of every tile, wait and meet the barriers, but skip the
+//    operand reads and the arithmetic (a second instantiation; G*S a multiple of 256 runs the
+//    code without the test).
 //  * Online softmax in the log2 domain; row max reduced across the two lane halves with
 //    v_permlane32_swap; the running max is only moved (and O rescaled) when a tile's max
 //    exceeds it by more than 2^8, which leaves the result unchanged and skips most
@@ -395,26 +399,29 @@ __device__ __forceinline__ void phase_barrier() {
 // needs tile j+1 at the coming barrier, group 1 needed it one barrier earlier); after the
 // vector phase 4 behind tile j+2 (group 1 needs it at the coming barrier, group 0 waits
 // for it half an iteration early). With U >= 0 (the stage of tile j, known at compile
-// time) every LDS operand read is a lane register plus an immediate offset.
+// time) every LDS operand read is a lane register plus an immediate offset. A wave whose
+// query rows all lie past the unit (act false) only copies, waits and meets the barriers.
 template <int U>
 __device__ __forceinline__ void steady_iter(int j, const char*& kp, const char*& vp, size_t tstep,
                                             uint32_t voff, uint32_t wrow, const LaneOffsets& lo,
                                             bf16x8 (&ka)[NDS], bf16x8 (&va)[NVO],
                                             const bf16x8 (&qreg)[NDS], WaveState& ws,
-                                            float scale_log2) {
+                                            float scale_log2, bool act) {
   const int s0 = U >= 0 ? U : (j & (NSTAGE - 1));
   const int s1 = (s0 + 1) & (NSTAGE - 1), sa = (s0 + NAHEAD) & (NSTAGE - 1);
   dma16u(kp, voff, (uint32_t)(uintptr_t)kst(sa) + wrow);
   dma16u(vp, voff, (uint32_t)(uintptr_t)vst(sa) + wrow);
   kp += tstep;
   vp += tstep;
-  matrix_phase(ka, va, qreg, ws, true, true);
+  if (act) matrix_phase(ka, va, qreg, ws, true, true);
   TT_WAIT_VM((NAHEAD - 1) * DMA_PER_TILE);
   phase_barrier();
-  load_k_ops(kst(s1), lo, ka);
-  load_v_ops(kst(s0), lo, va);
+  if (act) {
+    load_k_ops(kst(s1), lo, ka);
+    load_v_ops(kst(s0), lo, va);
+  }
   __builtin_amdgcn_sched_barrier(0);
-  vector_phase(ws, scale_log2, false, 0);
+  if (act) vector_phase(ws, scale_log2, false, 0);
   TT_WAIT_VM((NAHEAD - 2) * DMA_PER_TILE);
   phase_barrier();
 }
@@ -444,6 +451,9 @@ __device__ __forceinline__ int cluster_of(int x, int T, int NC) {
   return (int)ceil((double)(x + 1) * (double)NC / (double)T) - 1;
 }
 
+// ALL: every wave holds rows of the unit (G*S a multiple of the workgroup's 256 rows); else a
+// wave whose 32 rows all lie past the unit skips the operand reads and the arithmetic.
+template <bool ALL>
 __global__ __launch_bounds__(NTHR, 1) void attn_mfma_kernel(AttnArgs a) {
   int* wsum = reinterpret_cast<int*>(g_ring + NSTAGE * STAGEB);
 
@@ -487,6 +497,7 @@ __global__ __launch_bounds__(NTHR, 1) void attn_mfma_kernel(AttnArgs a) {
   const char* Qb = static_cast<const char*>(a.q);
   char* Ob = static_cast<char*>(a.o);
   const int G = a.G, S = a.S, rows_unit = G * S;
+  const bool act = ALL || __builtin_amdgcn_readfirstlane(qs * RWG + wave * RPW) < rows_unit;
 
   LaneOffsets lo;
   {
@@ -617,20 +628,20 @@ __global__ __launch_bounds__(NTHR, 1) void attn_mfma_kernel(AttnArgs a) {
     // iteration, the last ones and those whose copies need the block rows take the general
     // path below; the rest run steady_iter, eight at a time with compile-time stages.
     bf16x8 ka[NDS], va[NVO];
-    load_k_ops(kst(0), lo, ka);
+    if (act) load_k_ops(kst(0), lo, ka);
     if (grp == 1) {
       if (1 < n) wait_tiles_after(__builtin_amdgcn_readfirstlane(min(NAHEAD - 2, n - 2)));
       __syncthreads();
     }
     auto general_iter = [&](int j) {
       if (j + NAHEAD < n) issue_tile(src, ta + j + NAHEAD, (j + NAHEAD) & (NSTAGE - 1), wave);
-      matrix_phase(ka, va, qreg, ws, j < n, j >= 1);
+      if (act) matrix_phase(ka, va, qreg, ws, j < n, j >= 1);
       if (grp == 0 && j + 1 < n) wait_tiles_after(__builtin_amdgcn_readfirstlane(min(NAHEAD - 1, n - 2 - j)));
       phase_barrier();
-      if (j + 1 < n) load_k_ops(kst((j + 1) & (NSTAGE - 1)), lo, ka);
-      if (j < n) load_v_ops(kst(j & (NSTAGE - 1)), lo, va);
+      if (act && j + 1 < n) load_k_ops(kst((j + 1) & (NSTAGE - 1)), lo, ka);
+      if (act && j < n) load_v_ops(kst(j & (NSTAGE - 1)), lo, va);
       __builtin_amdgcn_sched_barrier(0);
-      if (j < n) vector_phase(ws, scale_log2, ta + j == nt - 1, nvalid - (ta + j) * KT);
+      if (act && j < n) vector_phase(ws, scale_log2, ta + j == nt - 1, nvalid - (ta + j) * KT);
       if (grp == 1 && j + 2 < n) wait_tiles_after(__builtin_amdgcn_readfirstlane(min(NAHEAD - 2, n - 3 - j)));
       phase_barrier();
     };
@@ -644,16 +655,16 @@ __global__ __launch_bounds__(NTHR, 1) void attn_mfma_kernel(AttnArgs a) {
       const char* vp = uniform_ptr(src.vc + (size_t)(ta + 1 + NAHEAD) * tstep);
       const uint32_t wrow = __builtin_amdgcn_readfirstlane(4 * wave * ROWB);
       for (; j + 7 <= jss; j += 8) {  // j % 8 == 1
-        steady_iter<1>(j, kp, vp, tstep, src.voff, wrow, lo, ka, va, qreg, ws, scale_log2);
-        steady_iter<2>(j + 1, kp, vp, tstep, src.voff, wrow, lo, ka, va, qreg, ws, scale_log2);
-        steady_iter<3>(j + 2, kp, vp, tstep, src.voff, wrow, lo, ka, va, qreg, ws, scale_log2);
-        steady_iter<4>(j + 3, kp, vp, tstep, src.voff, wrow, lo, ka, va, qreg, ws, scale_log2);
-        steady_iter<5>(j + 4, kp, vp, tstep, src.voff, wrow, lo, ka, va, qreg, ws, scale_log2);
-        steady_iter<6>(j + 5, kp, vp, tstep, src.voff, wrow, lo, ka, va, qreg, ws, scale_log2);
-        steady_iter<7>(j + 6, kp, vp, tstep, src.voff, wrow, lo, ka, va, qreg, ws, scale_log2);
-        steady_iter<0>(j + 7, kp, vp, tstep, src.voff, wrow, lo, ka, va, qreg, ws, scale_log2);
+        steady_iter<1>(j, kp, vp, tstep, src.voff, wrow, lo, ka, va, qreg, ws, scale_log2, act);
+        steady_iter<2>(j + 1, kp, vp, tstep, src.voff, wrow, lo, ka, va, qreg, ws, scale_log2, act);
+        steady_iter<3>(j + 2, kp, vp, tstep, src.voff, wrow, lo, ka, va, qreg, ws, scale_log2, act);
+        steady_iter<4>(j + 3, kp, vp, tstep, src.voff, wrow, lo, ka, va, qreg, ws, scale_log2, act);
+        steady_iter<5>(j + 4, kp, vp, tstep, src.voff, wrow, lo, ka, va, qreg, ws, scale_log2, act);
+        steady_iter<6>(j + 5, kp, vp, tstep, src.voff, wrow, lo, ka, va, qreg, ws, scale_log2, act);
+        steady_iter<7>(j + 6, kp, vp, tstep, src.voff, wrow, lo, ka, va, qreg, ws, scale_log2, act);
+        steady_iter<0>(j + 7, kp, vp, tstep, src.voff, wrow, lo, ka, va, qreg, ws, scale_log2, act);
       }
-      for (; j <= jss; ++j) steady_iter<-1>(j, kp, vp, tstep, src.voff, wrow, lo, ka, va, qreg, ws, scale_log2);
+      for (; j <= jss; ++j) steady_iter<-1>(j, kp, vp, tstep, src.voff, wrow, lo, ka, va, qreg, ws, scale_log2, act);
     }
     for (; j <= n; ++j) general_iter(j);
     if (grp == 0) __syncthreads();
@@ -767,7 +778,8 @@ size_t attn_part_bytes(int nc, int nq) { return (size_t)nc * 2 * nq * kPartBytes
 
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   if (ev0) (void)hipEventRecord(ev0, s);
-  hipLaunchKernelGGL(attn_mfma_kernel, dim3(a.NC * a.NQ), dim3(NTHR), 0, s, a);
+  if ((a.G * a.S) % RWG == 0) hipLaunchKernelGGL(attn_mfma_kernel<true>, dim3(a.NC * a.NQ), dim3(NTHR), 0, s, a);
+  else hipLaunchKernelGGL(attn_mfma_kernel<false>, dim3(a.NC * a.NQ), dim3(NTHR), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (ev1) (void)hipEventRecord(ev1, s);

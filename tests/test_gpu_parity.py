@@ -74,6 +74,10 @@ ATTN_CASES = [
     ("mfma-ragged", 3, 16, 32, 2, 128, [0, 77, 300], 320, W.BF16),
     ("mfma-tiny-rows", 2, 5, 6, 2, 128, [64, 129], 200, W.BF16),
     ("mfma-S1", 4, 1, 16, 1, 128, [1, 63, 64, 65], 70, W.BF16),
+    # units of fewer rows than a workgroup: the waves past the unit's rows idle
+    ("mfma-S4-idle-waves", 2, 4, 32, 2, 128, [300, 45], 320, W.BF16),      # 64 rows: 6 of 8 waves idle
+    ("mfma-S8-idle-waves", 2, 8, 32, 2, 128, [500, 0], 512, W.BF16),       # 128 rows
+    ("mfma-S24-NQ2-idle", 2, 24, 32, 2, 128, [400, 90], 400, W.BF16),      # 384 rows: second slice half idle
     ("mfma-S64-NQ8", 2, 64, 32, 2, 128, [500, 31], 512, W.BF16),
     ("mfma-S32-NQ2", 3, 32, 32, 2, 128, [700, 33, 260], 704, W.BF16),
     ("mfma-S128-NQ8", 1, 128, 32, 2, 128, [900], 900, W.BF16),
