@@ -80,7 +80,8 @@ def profiled_avg_us(kernel: str):
         return None
     import re
     m = re.search(r"attention source sha256\[:16\][^`]*`([0-9a-f]+)`", text)
-    t = re.search(r"\| " + kernel + r" \| \d+ \| ([0-9.]+) \|", text)
+    # (the kernel's name in the trace may carry its template argument, e.g. attn_mfma_kernel<true>)
+    t = re.search(r"\| " + kernel + r"(?:<[^|]*>)? \| \d+ \| ([0-9.]+) \|", text)
     if not m or not t or m.group(1) != attn_source_hash():
         return None
     return float(t.group(1))
