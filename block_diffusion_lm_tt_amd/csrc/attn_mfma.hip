@@ -710,10 +710,11 @@ __global__ __launch_bounds__(NTHR, 1) void attn_mfma_kernel(AttnArgs a) {
   }
 }
 
-// Merge the partials of every unit that a cluster boundary cut. Workgroup (y, c) reads the
-// merge record of cluster c (none: it exits) and covers 16 query rows of that unit (16
-// threads x 8 head-dim values per row). The pieces lie in clusters first .. c; they are
-// read eight at a time, all loads in flight together, and merged with a running max.
+// Merge the partials of every unit that a cluster boundary cut. Workgroup (x, u) reads the
+// merge record of unit u (none: the unit was held whole, and it exits) and covers 16 query
+// rows of that unit (16 threads x 8 head-dim values per row). The pieces lie in clusters
+// first .. last of the record; they are read eight at a time, all loads in flight together,
+// and merged with a running max.
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   constexpr int PB = 8;
   // grid: (row chunk, unit): the row chunks of one record are consecutive workgroups, so
