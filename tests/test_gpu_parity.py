@@ -78,6 +78,9 @@ ATTN_CASES = [
     ("mfma-S4-idle-waves", 2, 4, 32, 2, 128, [300, 45], 320, W.BF16),      # 64 rows: 6 of 8 waves idle
     ("mfma-S8-idle-waves", 2, 8, 32, 2, 128, [500, 0], 512, W.BF16),       # 128 rows
     ("mfma-S24-NQ2-idle", 2, 24, 32, 2, 128, [400, 90], 400, W.BF16),      # 384 rows: second slice half idle
+    ("mfma-G32-NQ2", 2, 16, 32, 1, 128, [260, 129], 260, W.BF16),          # one KV head: 512 rows, two slices
+    ("mfma-G5-S3", 3, 3, 10, 2, 128, [31, 32, 33], 40, W.BF16),            # odd group size, 15 rows
+    ("mfma-ctx-full", 4, 16, 32, 2, 128, [96, 96, 96, 96], 96, W.BF16),    # every context exactly Lmax
     ("mfma-S64-NQ8", 2, 64, 32, 2, 128, [500, 31], 512, W.BF16),
     ("mfma-S32-NQ2", 3, 32, 32, 2, 128, [700, 33, 260], 704, W.BF16),
     ("mfma-S128-NQ8", 1, 128, 32, 2, 128, [900], 900, W.BF16),
