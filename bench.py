@@ -773,7 +773,10 @@ def main():
         log(f"[bench] cpu baseline {cpu['value']:.3f} blocks/s on {cpu['cores']} threads")
 
     res = {
-        "metric": METRIC,
+        # the headline's metric name; other workloads and block sizes name their own S, context, dtype
+        "metric": METRIC if args.config == 3 and not args.block_size else
+        (f"denoise-attn blocks/sec + context-KV HBM GB/s (% peak), S={x.S} ctx {max(1, x.Lmax // 1024)}K "
+         f"{'bf16' if x.dtype == W.BF16 else 'f32'}"),
         "value": blocks_per_s,
         "unit": "blocks/s",
         "n_gpus": 1,
