@@ -43,48 +43,55 @@ def attn_flops(x) -> float:
     return float(4 * x.S * x.Hq * x.D * int(n.sum()))
 
 
-PROFILE_MD = os.path.join(ROOT, "profiles", "kernels_b32_s16_ctx8k_bf16.md")
+PROFILE_MD = "kernels_b32_s16_ctx8k_bf16.md"
+ATTN_SOURCES = ("attn_mfma.hip", "tt_internal.h")
+LMHEAD_MD = "kernels_lmhead_b32_s16_k4096_v131072.md"
+LMHEAD_SOURCES = ("lmhead.hip", "lmhead_exact.hip", "tt_internal.h")
 
 
-def attn_source_hash() -> str:
+def source_hash(files) -> str:
+    """First 16 hex digits of the SHA-256 over the given kernel sources, in order (the hash a
+    committed profile summary records for the sources it was taken on)."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("attn_mfma.hip", "tt_internal.h"):
+    for f in files:
         with open(os.path.join(ROOT, "block_diffusion_lm_tt_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def profiled_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from the committed counter summary (FETCH_SIZE and
-    WRITE_SIZE, each scaled by a plain copy's reading), or None when that summary was taken
-    on another version of the kernel source than the one built here."""
-    try:
-        text = open(PROFILE_MD).read()
-    except OSError:
-        return None
-    import re
-    m = re.search(r"attention source sha256\[:16\][^`]*`([0-9a-f]+)`", text)
-    t = re.search(kernel + r" traffic_bytes_per_launch: (\d+)", text)
-    if not m or not t or m.group(1) != attn_source_hash():
-        return None
-    return int(t.group(1))
+def attn_source_hash() -> str:
+    return source_hash(ATTN_SOURCES)
 
 
-def profiled_avg_us(kernel: str):
-    """The kernel's average duration in the committed rocprofv3 kernel-trace summary, when
-    that summary was taken on the kernel source built here (else None)."""
+def _profile_field(md: str, label: str, files, pattern: str):
+    """The first group of `pattern` in the committed summary profiles/<md>, when its recorded
+    `label` source hash equals the hash of `files` as built here (else None: a summary taken
+    on another version of the kernel says nothing about this one)."""
+    import re
     try:
-        text = open(PROFILE_MD).read()
+        text = open(os.path.join(ROOT, "profiles", md)).read()
     except OSError:
         return None
-    import re
-    m = re.search(r"attention source sha256\[:16\][^`]*`([0-9a-f]+)`", text)
-    # (the kernel's name in the trace may carry its template argument, e.g. attn_mfma_kernel<true>)
-    t = re.search(r"\| " + kernel + r"(?:<[^|]*>)? \| \d+ \| ([0-9.]+) \|", text)
-    if not m or not t or m.group(1) != attn_source_hash():
+    m = re.search(label + r" sha256\[:16\][^`]*`([0-9a-f]+)`", text)
+    t = re.search(pattern, text)
+    if not m or not t or m.group(1) != source_hash(files):
         return None
-    return float(t.group(1))
+    return t.group(1)
+
+
+def profiled_traffic(kernel: str, md: str = PROFILE_MD, label: str = "attention source", files=ATTN_SOURCES):
+    """HBM bytes per launch of `kernel` from a committed counter summary (FETCH_SIZE and
+    WRITE_SIZE, each scaled by a plain copy's reading), or None (see _profile_field)."""
+    v = _profile_field(md, label, files, kernel + r" traffic_bytes_per_launch: (\d+)")
+    return None if v is None else int(v)
+
+
+def profiled_avg_us(kernel: str, md: str = PROFILE_MD, label: str = "attention source", files=ATTN_SOURCES):
+    """The kernel's average duration in a committed rocprofv3 kernel-trace summary, or None.
+    (The kernel's name in the trace may carry its template argument, e.g. attn_mfma_kernel<true>.)"""
+    v = _profile_field(md, label, files, r"\| " + kernel + r"(?:<[^|]*>)? \| \d+ \| ([0-9.]+) \|")
+    return None if v is None else float(v)
 
 
 def cpu_baseline(w, budget_s: float) -> dict:
@@ -478,7 +485,9 @@ def lmhead_bench(args, torch, tt, TZ, W):
             if bound == "hbm" else
             {"bound": "mfma", "achieved": tfl, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
              "frac": tfl / MFMA_BF16_PEAK_TFLOPS})
-    roof.update({"kernel": "lmhead_reduce_kernel", "traffic": None, "avg_us": t_reduce * 1e6,
+    roof.update({"kernel": "lmhead_reduce_kernel",
+                 "traffic": profiled_traffic("lmhead_reduce_kernel", LMHEAD_MD, "LM-head source", LMHEAD_SOURCES),
+                 "avg_us": t_reduce * 1e6,
                  "algorithmic_bytes_per_launch": alg_bytes, "algorithmic_flop_per_launch": flops,
                  "hbm_frac": gbs / HBM_PEAK_GBS, "mfma_frac": tfl / MFMA_BF16_PEAK_TFLOPS})
     cpu = None
