@@ -37,8 +37,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int FT = 256;              // threads of the per-sequence kernels
 constexpr int kMaxS = 1024;
 constexpr double kZBand = 1e-4;      // the fp32 evaluation of Z, relative (about 1e-5)
-constexpr int EXB = 8;               // listed rows per pass of the exact kernel
-constexpr int KB = 512;              // features per LDS block of the exact kernel
+constexpr int EXB = 16;              // listed rows per pass of the exact kernel (a pass reads
+                                     // the tile's head rows once: more rows, fewer passes)
+constexpr int KB = 128;              // features per LDS block of the exact kernel
 
 __device__ __forceinline__ double bf(uint16_t x) { return (double)__uint_as_float(((uint32_t)x) << 16); }
 
@@ -162,6 +163,7 @@ __global__ __launch_bounds__(FT) void lmhead_flag_kernel(LmExactArgs a) {
 // One workgroup per 256-entry vocabulary tile; lane v of the tile accumulates, for up to EXB
 // listed rows at a time, sum_k h[k] w_v[k] in fp64 (hidden features staged in LDS as fp64,
 // read by broadcast), then each row's tile record is reduced over the workgroup.
+static_assert(EXB * KB * 8 + EXB * 256 * 8 <= 160 * 1024 - 4096, "exact kernel LDS");
 __global__ __launch_bounds__(256) void lmhead_exact_kernel(LmExactArgs a) {
   __shared__ double hs[EXB][KB];
   __shared__ double lg[EXB][256];
