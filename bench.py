@@ -47,6 +47,8 @@ PROFILE_MD = "kernels_b32_s16_ctx8k_bf16.md"
 ATTN_SOURCES = ("attn_mfma.hip", "tt_internal.h")
 LMHEAD_MD = "kernels_lmhead_b32_s16_k4096_v131072.md"
 LMHEAD_SOURCES = ("lmhead.hip", "lmhead_exact.hip", "tt_internal.h")
+MAMBA_MD = "kernels_mamba2_b32_s16_h128_p64_n128_bf16.md"
+MAMBA_SOURCES = ("mamba.hip", "adaln.hip", "tt_internal.h")
 
 
 def source_hash(files) -> str:
@@ -616,8 +618,11 @@ def mamba_bench(args, torch, tt, TZ, W):
            "scan_with_state_out_GBps": (alg + state_bytes) / t_state / 1e9,
            "adaln_modulate_us_per_call": t_mod * 1e6, "adaln_modulate_GBps": ad_mod / t_mod / 1e9,
            "adaln_gate_us_per_call": t_gate * 1e6, "adaln_gate_GBps": ad_gate / t_gate / 1e9,
-           "roofline": {"kernel": "mamba2_scan_kernel", "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
-                        "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None, "avg_us": t_scan * 1e6,
+           # (bf16 activations with these P and N take the matrix-core scan)
+           "roofline": {"kernel": "mamba2_scan_mfma_kernel", "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                        "traffic": profiled_traffic("mamba2_scan_mfma_kernel", MAMBA_MD, "scan source", MAMBA_SOURCES),
+                        "avg_us": t_scan * 1e6,
                         "algorithmic_bytes_per_launch": alg, "readout_flop_per_launch": flop,
                         "frac_of_measured_stream_read": gbs / stream["GBps"],
                         "frac_of_same_size_stream_read": same["us"] / (t_scan * 1e6)},
